@@ -1,0 +1,211 @@
+"""Python binding of libmoe_mi355x.so: one GPU's share of a Mixture-of-Experts
+layer (top-k router, dispatch, grouped Linear-1 + SwiGLU, grouped Linear-2,
+weighted combine) as hand-written HIP kernels for MI355X (gfx950).
+
+The functions here only marshal arguments: torch tensors (device memory) and
+torch's current HIP stream go to the C ABI declared in include/moe_mi355x.h,
+under the same names without the `moe_` prefix. Every step of the layer runs
+in the library's kernels; there is no fallback. If the library is missing the
+import fails with an error naming the build command.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+__all__ = [
+    "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
+    "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
+    "check_workspace", "SCHED", "DTYPE", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
+          4: "MOE_ERR_HIP", 5: "MOE_ERR_DEADLOCK"}
+SCHED = {"separate": 0, "expert_wave": 1, "interleaved": 2}
+DTYPE = {"bf16": 0, "fp8_e4m3": 1}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == 4:
+            msg += f" (hipError {lib().moe_last_hip_error()})"
+        super().__init__(msg)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "d", "f", "E_global", "k", "e_begin", "e_end", "dtype", "quant_block", "num_segments", "sched",
+        "lead_D", "wave_experts", "grid")] + [("flags", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "topk_idx", "topk_w", "counts", "offsets", "row_src", "row_dst", "tok_off", "comb_w", "x_perm",
+        "x_perm_scale", "h", "h_scale", "combine_buf", "meta", "total")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m expert_grouped_gemm_amd.build` "
+                              f"(hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        PP = ctypes.POINTER(Problem)
+        L.moe_workspace_size.restype = ctypes.c_size_t
+        L.moe_workspace_size.argtypes = [PP]
+        L.moe_workspace_get_layout.restype = ctypes.c_int
+        L.moe_workspace_get_layout.argtypes = [PP, ctypes.POINTER(WorkspaceLayout)]
+        L.moe_route_topk.restype = ctypes.c_int
+        L.moe_route_topk.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_dispatch.restype = ctypes.c_int
+        L.moe_dispatch.argtypes = [PP] + [_P] * 13 + [ctypes.c_size_t, _P]
+        L.moe_expert_forward.restype = ctypes.c_int
+        L.moe_expert_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine.argtypes = [PP, _P, _P, _P, _P, _P, _P]
+        L.moe_layer_forward.restype = ctypes.c_int
+        L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.moe_check_workspace.restype = ctypes.c_int
+        L.moe_check_workspace.argtypes = [PP, _P, ctypes.c_size_t, _P]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_last_hip_error.restype = ctypes.c_int
+        L.moe_last_hip_error.argtypes = []
+        L.moe_version.restype = ctypes.c_char_p
+        L.moe_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def make_problem(T: int, d: int, f: int, E_global: int, k: int, e_begin: int = 0, e_end: Optional[int] = None,
+                 dtype: str = "bf16", num_segments: int = 1, sched: str = "interleaved", lead_D: int = 0,
+                 wave_experts: int = 0, grid: int = 0, quant_block: int = 128) -> Problem:
+    return Problem(T=T, d=d, f=f, E_global=E_global, k=k, e_begin=e_begin,
+                   e_end=E_global if e_end is None else e_end, dtype=DTYPE[dtype], quant_block=quant_block,
+                   num_segments=num_segments, sched=SCHED[sched], lead_D=lead_D, wave_experts=wave_experts,
+                   grid=grid, flags=0)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoEError(status, where)
+
+
+def workspace_size(p: Problem) -> int:
+    n = lib().moe_workspace_size(ctypes.byref(p))
+    if n == 0:
+        raise MoEError(2, "moe_workspace_size")
+    return n
+
+
+def workspace_layout(p: Problem) -> WorkspaceLayout:
+    out = WorkspaceLayout()
+    _check(lib().moe_workspace_get_layout(ctypes.byref(p), ctypes.byref(out)), "moe_workspace_get_layout")
+    return out
+
+
+def alloc_workspace(p: Problem, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Typed views of the intermediates a moe_layer_forward call leaves in `ws`."""
+    L = workspace_layout(p)
+    El = p.e_end - p.e_begin
+    cap = p.T * min(p.k, El)
+    esz = 1 if p.dtype == DTYPE["fp8_e4m3"] else 2
+    edt = torch.uint8 if esz == 1 else torch.bfloat16
+
+    def view(off, n, dt, shape):
+        nbytes = n * torch.empty((), dtype=dt).element_size()
+        return ws[off:off + nbytes].view(dt).view(shape)
+
+    v = dict(
+        topk_idx=view(L.topk_idx, p.T * p.k, torch.int32, (p.T, p.k)),
+        topk_w=view(L.topk_w, p.T * p.k, torch.float32, (p.T, p.k)),
+        counts=view(L.counts, El, torch.int32, (El,)),
+        offsets=view(L.offsets, El + 1, torch.int32, (El + 1,)),
+        row_src=view(L.row_src, cap, torch.int32, (cap,)),
+        row_dst=view(L.row_dst, cap, torch.int32, (cap,)),
+        tok_off=view(L.tok_off, p.T + 1, torch.int32, (p.T + 1,)),
+        comb_w=view(L.comb_w, cap, torch.float32, (cap,)),
+        x_perm=view(L.x_perm, cap * p.d, edt, (cap, p.d)),
+        h=view(L.h, cap * p.f, edt, (cap, p.f)),
+        combine_buf=view(L.combine_buf, cap * p.d, torch.float32, (cap, p.d)),
+        meta=view(L.meta, 64, torch.int32, (64,)),
+    )
+    if esz == 1:
+        v["x_perm_scale"] = view(L.x_perm_scale, cap * (p.d // 128), torch.float32, (p.d // 128, cap))
+        v["h_scale"] = view(L.h_scale, cap * (p.f // 128), torch.float32, (p.f // 128, cap))
+    return v
+
+
+def route_topk(p: Problem, logits, topk_idx, topk_w, counts_global=None, stream=None):
+    _check(lib().moe_route_topk(ctypes.byref(p), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts_global),
+                                _stream(stream)), "moe_route_topk")
+
+
+def dispatch(p: Problem, X, X_scale, topk_idx, topk_w, counts, offsets, row_src, row_dst, tok_off, comb_w,
+             X_perm, X_perm_scale, workspace, stream=None):
+    _check(lib().moe_dispatch(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                              _ptr(offsets), _ptr(row_src), _ptr(row_dst), _ptr(tok_off), _ptr(comb_w),
+                              _ptr(X_perm), _ptr(X_perm_scale), _ptr(workspace), workspace.numel(),
+                              _stream(stream)), "moe_dispatch")
+
+
+def expert_forward(p: Problem, X_perm, X_perm_scale, offsets, row_dst, W1, W1_scale, W2, W2_scale, combine_buf,
+                   workspace, stream=None):
+    _check(lib().moe_expert_forward(ctypes.byref(p), _ptr(X_perm), _ptr(X_perm_scale), _ptr(offsets),
+                                    _ptr(row_dst), _ptr(W1), _ptr(W1_scale), _ptr(W2), _ptr(W2_scale),
+                                    _ptr(combine_buf), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_expert_forward")
+
+
+def combine(p: Problem, combine_buf, tok_off, comb_w, Y, Y_fp32=None, stream=None):
+    _check(lib().moe_combine(ctypes.byref(p), _ptr(combine_buf), _ptr(tok_off), _ptr(comb_w), _ptr(Y), _ptr(Y_fp32),
+                             _stream(stream)), "moe_combine")
+
+
+def layer_forward(p: Problem, X, X_scale, logits, W1, W1_scale, W2, W2_scale, Y, Y_fp32, workspace, stream=None):
+    _check(lib().moe_layer_forward(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(logits), _ptr(W1), _ptr(W1_scale),
+                                   _ptr(W2), _ptr(W2_scale), _ptr(Y), _ptr(Y_fp32), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)), "moe_layer_forward")
+
+
+def check_workspace(p: Problem, workspace, stream=None):
+    _check(lib().moe_check_workspace(ctypes.byref(p), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_check_workspace")

@@ -1,0 +1,195 @@
+// Host side of the C ABI declared in include/moe_mi355x.h: argument checks,
+// workspace layout and the launch order of the share's stages (route ->
+// dispatch -> grouped expert GEMM -> combine) on the caller's stream.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+moe_status_t hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_INTERLEAVED) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->flags != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->lead_D < 0 || p->wave_experts < 0 || p->grid < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->T < 1 || p->d < 1 || p->f < 1 || p->E_global < 1 || p->k < 1) return MOE_ERR_UNSUPPORTED;
+  if (p->E_global > 1024 || p->k > 16 || p->k > p->E_global) return MOE_ERR_UNSUPPORTED;
+  if (p->e_begin < 0 || p->e_begin >= p->e_end || p->e_end > p->E_global) return MOE_ERR_UNSUPPORTED;
+  if (p->num_segments < 1 || p->T % p->num_segments) return MOE_ERR_UNSUPPORTED;
+  if (p->d % 128 || p->f % 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t El = p->e_end - p->e_begin;
+  const int64_t cap = (int64_t)p->T * (p->k < El ? p->k : El);
+  // 32-bit row and element indices inside the kernels
+  if ((int64_t)p->T * p->k > (1ll << 30) || cap * p->d > (1ll << 31) - 1 || cap * p->f > (1ll << 31) - 1)
+    return MOE_ERR_UNSUPPORTED;
+  if (p->dtype == MOE_DTYPE_FP8_E4M3) {
+    if (p->quant_block != 128 || p->f % 128 || p->T % 128) return MOE_ERR_UNSUPPORTED;
+    return MOE_ERR_UNSUPPORTED;  // the fp8 expert kernels are not built yet
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_ws(const moe::Layout& L, const void* ws, size_t bytes) {
+  if (!ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_INVALID_ARGUMENT;
+  if (bytes < L.pub.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+MOE_API size_t moe_workspace_size(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return moe::make_layout(*p).pub.total;
+}
+
+MOE_API moe_status_t moe_workspace_get_layout(const moe_problem_t* p, moe_workspace_layout_t* out) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARGUMENT;
+  *out = moe::make_layout(*p).pub;
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_route_topk(const moe_problem_t* p, const float* logits, int32_t* topk_idx,
+                                    float* topk_w, int32_t* counts_global, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  hipError_t e = moe::launch_route(*p, logits, topk_idx, topk_w, counts_global, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const float* X_scale,
+                                  const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                                  float* comb_w, void* X_perm, float* X_perm_scale, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (!X || !topk_idx || !topk_w || !counts || !offsets || !row_src || !row_dst || !tok_off || !comb_w ||
+      !X_perm)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_scale != nullptr) || fp8 != (X_perm_scale != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(X) || !aligned16(X_perm)) return MOE_ERR_INVALID_ARGUMENT;
+  moe::Layout L = moe::make_layout(*p);
+  if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
+  hipError_t e = moe::launch_dispatch(*p, L, static_cast<char*>(workspace), X, X_scale, topk_idx, topk_w, counts,
+                                      offsets, row_src, row_dst, tok_off, comb_w, X_perm, X_perm_scale,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
+                                        const int32_t* offsets, const int32_t* row_dst, const void* W1,
+                                        const float* W1_scale, const void* W2, const float* W2_scale,
+                                        float* combine_buf, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (!X_perm || !offsets || !row_dst || !W1 || !W2 || !combine_buf) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_perm_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(X_perm) || !aligned16(W1) || !aligned16(W2) || !aligned16(combine_buf))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe::Layout L = moe::make_layout(*p);
+  if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
+  hipError_t e = moe::launch_expert_forward(*p, L, static_cast<char*>(workspace), X_perm, X_perm_scale, offsets,
+                                            row_dst, W1, W1_scale, W2, W2_scale, combine_buf,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const float* combine_buf, const int32_t* tok_off,
+                                 const float* comb_w, void* Y, float* Y_fp32, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!combine_buf || !tok_off || !comb_w || !Y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(combine_buf) || !aligned16(Y) || (Y_fp32 && !aligned16(Y_fp32))) return MOE_ERR_INVALID_ARGUMENT;
+  hipError_t e = moe::launch_combine(*p, combine_buf, tok_off, comb_w, Y, Y_fp32, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
+                                       const float* logits, const void* W1, const float* W1_scale,
+                                       const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (!X || !logits || !W1 || !W2 || !Y) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || (Y_fp32 && !aligned16(Y_fp32)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe::Layout L = moe::make_layout(*p);
+  if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const moe_workspace_layout_t& W = L.pub;
+  hipError_t e = moe::launch_route(*p, logits, I(W.topk_idx), F(W.topk_w), nullptr, s);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch(*p, L, ws, X, X_scale, I(W.topk_idx), F(W.topk_w), I(W.counts), I(W.offsets),
+                             I(W.row_src), I(W.row_dst), I(W.tok_off), F(W.comb_w), ws + W.x_perm,
+                             fp8 ? F(W.x_perm_scale) : nullptr, s);
+  if (e == hipSuccess)
+    e = moe::launch_expert_forward(*p, L, ws, ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, I(W.offsets),
+                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, F(W.combine_buf), s);
+  if (e == hipSuccess) e = moe::launch_combine(*p, F(W.combine_buf), I(W.tok_off), F(W.comb_w), Y, Y_fp32, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  moe::Layout L = moe::make_layout(*p);
+  if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.pub.meta) + moe::META_ERR;
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (host) {
+    const int32_t zero = 0;
+    e = hipMemcpyAsync(flag, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    return MOE_ERR_DEADLOCK;
+  }
+  return MOE_OK;
+}
+
+MOE_API const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported problem shape";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_DEADLOCK: return "persistent pipeline wait timed out";
+  }
+  return "unknown status";
+}
+
+MOE_API int moe_last_hip_error(void) { return g_last_hip_error; }
+
+MOE_API const char* moe_version(void) { return "0.1.0"; }
+
+}  // extern "C"

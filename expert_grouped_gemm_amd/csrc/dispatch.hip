@@ -1,0 +1,222 @@
+// Dispatch of the local share as an on-GPU permutation: Cui et al., "Fine-
+// grained Computation-Communication Overlap via Tile-level Signaling and
+// Scheduling for MoE", Section 2.1 step (2) (tokens go to the experts that
+// host them) and Section 3.2 (per-expert row layout built before the grouped
+// GEMM); X-Stage, Section 2.2 (Dispatch precedes Linear-1).
+//
+// Assignment a = t*k + j is local when topk_idx[a] lies in [e_begin, e_end).
+// Rows of one expert are ordered by ascending a (a stable counting sort), so
+// the permutation is unique and needs no atomics:
+//   1. count   : one wavefront per chunk of assignments, LDS histogram of
+//                local experts -> blk_counts[chunk][e]
+//   2. scan    : one block; per-expert totals, offsets, per-chunk bases;
+//                per-output-row local counts -> tok_off (exclusive scan)
+//   3. scatter : one wavefront per chunk, walking its assignments in order;
+//                the rank of an assignment among equal experts in a group of
+//                64 comes from a ballot over lanes (a match-any loop), the
+//                running base per expert from LDS.
+//   4. gather  : X_perm[r] = X[row_src[r] / k], 16-byte lanes, coalesced.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t* __restrict__ idx, int Tk, int chunk,
+                                                            int e_begin, int El,
+                                                            int32_t* __restrict__ blk_counts) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < El; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * chunk;
+  const int a1 = min(Tk, a0 + chunk);
+  for (int a = a0 + threadIdx.x; a < a1; a += 64) {
+    const int e = idx[a] - e_begin;
+    if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += 64) blk_counts[(size_t)blockIdx.x * El + e] = hist[e];
+}
+
+// Exclusive scan over a 1024-thread block; returns the exclusive prefix of v
+// and the block total in *total.
+__device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    int s = sh[threadIdx.x];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(s, off, 16);
+      if ((int)threadIdx.x >= off) s += y;
+    }
+    sh[16 + threadIdx.x] = s;  // inclusive over waves
+  }
+  __syncthreads();
+  const int wave_base = wv ? sh[16 + wv - 1] : 0;
+  *total = sh[16 + 15];
+  const int r = wave_base + x - v;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                             int S, int e_begin, int El, int nblk,
+                                                             int32_t* __restrict__ blk_counts,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tok_off,
+                                                             int32_t* __restrict__ meta) {
+  __shared__ int sh[64];
+  // per-expert totals and per-chunk exclusive bases (thread e owns expert e)
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < El) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_counts[(size_t)b * El + e];
+      blk_counts[(size_t)b * El + e] = tot;
+      tot += c;
+    }
+  }
+  int A;
+  const int off = block_exclusive_scan_1024(e < El ? tot : 0, sh, &A);
+  if (e < El) {
+    counts[e] = tot;
+    offsets[e] = off;
+    for (int b = 0; b < nblk; ++b) blk_counts[(size_t)b * El + e] += off;
+  }
+  if (e == 0) {
+    offsets[El] = A;
+    meta[META_A] = A;
+  }
+  // per-output-row local counts, scanned in row order q
+  const int per = (T + 1023) / 1024;
+  const int q0 = threadIdx.x * per;
+  const int seg = T / S;
+  int run = 0;
+  for (int q = q0; q < min(T, q0 + per); ++q) {
+    const int t = (q % seg) * S + q / seg;
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
+    run += c;
+  }
+  int total;
+  int base = block_exclusive_scan_1024(run, sh, &total);
+  for (int q = q0; q < min(T, q0 + per); ++q) {
+    const int t = (q % seg) * S + q / seg;
+    tok_off[q] = base;
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
+    base += c;
+  }
+  if (threadIdx.x == 0) tok_off[T] = total;
+}
+
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ w, int T, int k, int S,
+                                                              int chunk, int e_begin, int El,
+                                                              const int32_t* __restrict__ blk_base,
+                                                              const int32_t* __restrict__ tok_off,
+                                                              int32_t* __restrict__ row_src,
+                                                              int32_t* __restrict__ row_dst,
+                                                              float* __restrict__ comb_w) {
+  extern __shared__ int32_t running[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < El; e += 64) running[e] = blk_base[(size_t)blockIdx.x * El + e];
+  __syncthreads();
+  const int Tk = T * k;
+  const int a0 = blockIdx.x * chunk;
+  const int a1 = min(Tk, a0 + chunk);
+  const int seg = T / S;
+  for (int g = a0; g < a1; g += 64) {
+    const int a = g + lane;
+    const int e = (a < a1) ? idx[a] - e_begin : -1;
+    const bool local = (unsigned)e < (unsigned)El;
+    uint64_t pending = __ballot(local);
+    int pos = 0;
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int v = __shfl(e, leader, 64);
+      const uint64_t same = __ballot(local && e == v);
+      const int base = running[v];
+      if (local && e == v) {
+        const uint64_t below = same & ((1ull << lane) - 1ull);
+        pos = base + __popcll(below);
+      }
+      __syncthreads();
+      if (lane == leader) running[v] = base + __popcll(same);
+      __syncthreads();
+      pending &= ~same;
+    }
+    if (local) {
+      const int t = a / k, j = a - t * k;
+      int before = 0;
+      for (int jj = 0; jj < j; ++jj) before += (unsigned)(idx[(size_t)t * k + jj] - e_begin) < (unsigned)El;
+      const int slot = tok_off[y_row_of_token(t, T, S)] + before;
+      row_src[pos] = a;
+      row_dst[pos] = slot;
+      comb_w[slot] = w[a];
+    }
+  }
+  (void)seg;
+}
+
+// X_perm[r, :] = X[row_src[r] / k, :] for r < A; fp8 also gathers the row's
+// block scales: X_perm_scale[c * cap + r] = X_scale[(t / 128) * (d / 128) + c].
+__global__ __launch_bounds__(256) void dispatch_gather_kernel(const uint8_t* __restrict__ X,
+                                                              const float* __restrict__ X_scale, int k,
+                                                              int row_bytes, int dblocks, int cap,
+                                                              const int32_t* __restrict__ row_src,
+                                                              const int32_t* __restrict__ meta,
+                                                              uint8_t* __restrict__ X_perm,
+                                                              float* __restrict__ X_perm_scale) {
+  const int A = meta[META_A];
+  const int vecs = row_bytes >> 4;
+  for (int r = blockIdx.x; r < A; r += gridDim.x) {
+    const int t = row_src[r] / k;
+    const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)t * row_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(X_perm + (size_t)r * row_bytes);
+    for (int i = threadIdx.x; i < vecs; i += blockDim.x) dst[i] = src[i];
+    if (X_scale) {
+      for (int c = threadIdx.x; c < dblocks; c += blockDim.x)
+        X_perm_scale[(size_t)c * cap + r] = X_scale[(size_t)(t >> 7) * dblocks + c];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, const void* X,
+                           const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,
+                           int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                           float* comb_w, void* X_perm, float* X_perm_scale, hipStream_t s) {
+  const int Tk = p.T * p.k;
+  const int El = L.E_l;
+  int32_t* blk = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+  int32_t* meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nblk), dim3(64), El * 4, s, idx, Tk, L.chunk, p.e_begin, El,
+                     blk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, idx, p.T, p.k, p.num_segments, p.e_begin,
+                     El, L.nblk, blk, counts, offsets, tok_off, meta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nblk), dim3(64), El * 4, s, idx, w, p.T, p.k,
+                     p.num_segments, L.chunk, p.e_begin, El, blk, tok_off, row_src, row_dst, comb_w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const int row_bytes = p.d * (fp8 ? 1 : 2);
+  const int blocks = L.cap < 8192 ? (L.cap > 0 ? L.cap : 1) : 8192;
+  hipLaunchKernelGGL(dispatch_gather_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(X),
+                     fp8 ? X_scale : nullptr, p.k, row_bytes, p.d / 128, L.cap, row_src, meta,
+                     static_cast<uint8_t*>(X_perm), X_perm_scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,483 @@
+// Persistent grouped expert GEMM with a SwiGLU Linear-1 epilogue and a
+// combine-store Linear-2 epilogue, on gfx950 bf16 MFMA.
+//
+// What it computes (X-Stage: An Overlooked Pipeline Stage for Communication-
+// Computation Overlap in DiT Inference, Section 2.2 "MegaMoE Execution"):
+// per local expert e and expert-contiguous row r of X_perm,
+//   Linear-1 + SwiGLU : H[r, j]  = bf16( silu(W1[e][j] . x_r) * (W1[e][f+j] . x_r) )
+//   Linear-2          : C[row_dst[r], n] = W2[e][n] . H[r]          (fp32)
+//
+// How the work is cut (Cui et al., Section 3.3.1: one rank-wide persistent
+// kernel walks a unified tile list, each item an (expert, tile) pair, with
+// the expert's pointers substituted per item; X-Stage Algorithm 1 for the
+// ordering):
+//   - a row band p is up to kBM = 256 consecutive rows of one expert; bands
+//     are listed expert by expert (row p of the scheduler);
+//   - a Linear-1 tile is (p, n1): 64 SwiGLU columns = 64 gate + 64 up rows of
+//     W1[e]; a Linear-2 tile is (p, n2): 128 output columns;
+//   - the K loop streams 128-byte slices of every row through a three-stage
+//     LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4),
+//     so the weight tile is read from HBM once per band and reused by every
+//     row of the band;
+//   - 4 wavefronts, 2 (rows) x 2 (columns); a wavefront owns the 32-row
+//     blocks {wm, wm+2, ...} of the band and two 32-column blocks, one
+//     v_mfma_f32_32x32x16_bf16 accumulator each; the number of 32-row blocks
+//     is a template parameter, so empty blocks cost neither loads nor MFMAs.
+//
+// Schedules (X-Stage Section 4.2, Algorithm 1, Figure 4):
+//   MODE_SEP_L1/L2    every Linear-1 tile, then (next launch) every Linear-2 tile
+//   MODE_WAVE         experts grouped into waves; a wave's Linear-1 tiles, then
+//                     its Linear-2 tiles; each Linear-2 tile waits on l2_full[p]
+//   MODE_INTERLEAVED  per pair-instance g (two workgroups, roles r = 0, 1) two
+//                     cursors k1, k2 advance by the instance count; a Linear-2
+//                     tile of row p2 = k2 / P2 is emitted only when the Linear-1
+//                     row p1 = k1 / P1 leads it by at least D rows, otherwise
+//                     the next Linear-1 tile; the N-tile of a pair cursor is
+//                     n = 2 (k mod P) + r.
+// l2_full[p] counts stored Linear-1 tiles of row p (X-Stage Section 4.2,
+// "Condition 2"): the Linear-1 epilogue publishes with an agent-scope release
+// after its H stores, a Linear-2 tile of row p acquires once it reaches the
+// number of Linear-1 tiles per row. A workgroup only waits on rows at least
+// D >= 1 behind its own Linear-1 cursor, so the smallest unfinished Linear-1
+// row always belongs to a workgroup that is not waiting (no deadlock while
+// the whole grid is resident: one workgroup per CU). Waits are bounded; a
+// timeout sets the sticky error flag meta[META_ERR].
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t lds_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+struct GemmParams {
+  const uint8_t* X;       // X_perm [cap, d] bf16
+  const uint8_t* W1;      // [E_l, 2f, d]
+  const uint8_t* W2;      // [E_l, d, f]
+  uint8_t* H;             // [cap, f]
+  float* C;               // combine_buf [cap, d]
+  const int32_t* row_dst;
+  const int32_t* band_expert;
+  const int32_t* band_row0;
+  const int32_t* band_rows;
+  int32_t* l2_full;
+  int32_t* meta;
+  const int32_t* wave_band0;
+  int d, f;
+  int N1, N2;             // Linear-1 tiles per row band (f / 64), Linear-2 tiles (d / 128)
+  int mode;
+  int lead_D;
+};
+
+struct Tile {
+  const uint8_t* A;       // first row of the band (X_perm or H)
+  const uint8_t* Bg;      // weight rows 0..63 of the tile
+  const uint8_t* Bu;      // weight rows 64..127 of the tile
+  size_t lda, ldb;        // row pitch in bytes
+  int rows;               // valid rows of the band (1..256)
+  int row0;               // first X_perm / H row of the band
+  int n;                  // N-tile index
+  int ktiles;             // K / 64
+};
+
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kKBytes + ((chunk ^ (row & 7)) << 4); }
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() would also
+// drain every outstanding global load (vmcnt(0)), which would empty the
+// prefetch ring; global->LDS completion is tracked explicitly with
+// wait_vmcnt instead.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One pipeline stage: K bytes [kt*128, kt*128+128) of the band's first 32*MB
+// rows and of the tile's 128 weight rows. Every lane issues MB + 4 loads of 16
+// bytes; lane i of an instruction lands at LDS base + 16*i (8 rows of 128 B).
+template <int MB>
+__device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kb = kt * kKBytes;
+  const int sub = lane >> 3, slot = lane & 7;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r0 = (i * 4 + w) * 8;
+    const int r = r0 + sub;
+    const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
+    const uint8_t* g = t.A + (size_t)gr * t.lda + kb + ((slot ^ (r & 7)) << 4);
+    __builtin_amdgcn_global_load_lds(g, st + r0 * kKBytes, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r0 = (i * 4 + w) * 8;
+    const int r = r0 + sub;
+    const uint8_t* base = r < 64 ? t.Bg : t.Bu;
+    const uint8_t* g = base + (size_t)(r & 63) * t.ldb + kb + ((slot ^ (r & 7)) << 4);
+    __builtin_amdgcn_global_load_lds(g, st + kStageA + r0 * kKBytes, 16, 0, 0);
+  }
+}
+
+// MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
+// and weight rows {nb*64 + wn*32 .. +32} for nb = 0, 1.
+template <int NMB>
+__device__ __forceinline__ void compute_stage(const lds_t* st, int wm, int wn, f32x16 (&acc)[NMB][2]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int chunk = ks * 2 + hi;
+    bf16x8 b[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      b[nb] = *(const lds_bf16x8*)(st + kStageA + lds_off(nb * 64 + wn * 32 + lr, chunk));
+#pragma unroll
+    for (int mi = 0; mi < NMB; ++mi) {
+      const int row = (wm + 2 * mi) * 32 + lr;
+      const bf16x8 a = *(const lds_bf16x8*)(st + lds_off(row, chunk));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mi][nb], 0, 0, 0);
+    }
+  }
+}
+
+// Accumulator element i of a 32x32 block sits at row 8*(i/4) + 4*(lane/32) + i%4,
+// column lane%32.
+template <int NMB, bool L1>
+__device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int wm, int wn,
+                                         const f32x16 (&acc)[NMB][2]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    const int mb = wm + 2 * mi;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+      if (m < t.rows) {
+        if constexpr (L1) {
+          const float g = acc[mi][0][i], u = acc[mi][1][i];
+          const float act = g / (1.0f + expf(-g)) * u;
+          const int col = t.n * kBN1 + wn * 32 + lr;
+          reinterpret_cast<uint16_t*>(P.H)[(size_t)(t.row0 + m) * P.f + col] = f32_to_bf16_rne(act);
+        } else {
+          const int dst = P.row_dst[t.row0 + m];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = t.n * kBN2 + nb * 64 + wn * 32 + lr;
+            P.C[(size_t)dst * P.d + col] = acc[mi][nb][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+// The whole tile for one wavefront role: every wavefront runs the same number
+// of loads and barriers; NMB (its share of the MB row blocks) only changes the
+// MFMA and epilogue work, and the accumulators stay inside this function.
+template <int MB, int NMB, bool L1>
+__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds, int wm, int wn) {
+  f32x16 acc[NMB > 0 ? NMB : 1][2];
+#pragma unroll
+  for (int a = 0; a < (NMB > 0 ? NMB : 1); ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  // K >= 128 bytes * 2 stages is guaranteed by the shape checks (d, f % 128 == 0).
+  const int KT = t.ktiles;
+  lds_t* s0 = lds;
+  lds_t* s1 = lds + kStageBytes;
+  lds_t* s2 = lds + 2 * kStageBytes;
+  issue_stage<MB>(t, 0, s0);
+  issue_stage<MB>(t, 1, s1);
+  for (int kt = 0; kt + 2 < KT; ++kt) {
+    wait_vmcnt<MB + 4>();    // this lane's loads of stage kt have landed
+    lds_barrier();           // ... everyone's; and stage kt-1 (in s2) is no longer read
+    issue_stage<MB>(t, kt + 2, s2);
+    if constexpr (NMB > 0) compute_stage<NMB>(s0, wm, wn, acc);
+    lds_t* r = s0;
+    s0 = s1;
+    s1 = s2;
+    s2 = r;
+  }
+  wait_vmcnt<MB + 4>();
+  lds_barrier();
+  if constexpr (NMB > 0) compute_stage<NMB>(s0, wm, wn, acc);
+  wait_vmcnt<0>();
+  lds_barrier();
+  if constexpr (NMB > 0) compute_stage<NMB>(s1, wm, wn, acc);
+  __syncthreads();  // LDS ring free for the next tile
+  if constexpr (NMB > 0) epilogue<NMB, L1>(P, t, wm, wn, acc);
+}
+
+template <int MB, bool L1>
+__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+  const int w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  if (wm == 0) tile_body<MB, (MB + 1) / 2, L1>(P, t, lds, wm, wn);
+  else tile_body<MB, MB / 2, L1>(P, t, lds, wm, wn);
+}
+
+template <bool L1>
+__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+  switch ((t.rows + 31) >> 5) {
+    case 1: run_tile<1, L1>(P, t, lds); break;
+    case 2: run_tile<2, L1>(P, t, lds); break;
+    case 3: run_tile<3, L1>(P, t, lds); break;
+    case 4: run_tile<4, L1>(P, t, lds); break;
+    case 5: run_tile<5, L1>(P, t, lds); break;
+    case 6: run_tile<6, L1>(P, t, lds); break;
+    case 7: run_tile<7, L1>(P, t, lds); break;
+    default: run_tile<8, L1>(P, t, lds); break;
+  }
+}
+
+__device__ __forceinline__ void wait_row_ready(const GemmParams& P, int p) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&P.l2_full[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < P.N1) {
+      // after one timeout in this call every later wait gives up at once
+      if (__hip_atomic_load(&P.meta[META_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(&P.meta[META_ERR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ void publish_row(const GemmParams& P, int p) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&P.l2_full[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool L1>
+__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, bool fused, lds_t* lds) {
+  Tile t;
+  const int e = P.band_expert[p];
+  t.row0 = P.band_row0[p];
+  t.rows = P.band_rows[p];
+  t.n = n;
+  if constexpr (L1) {
+    t.lda = (size_t)P.d * 2;
+    t.ldb = (size_t)P.d * 2;
+    t.A = P.X + (size_t)t.row0 * t.lda;
+    const uint8_t* We = P.W1 + (size_t)e * 2 * P.f * t.ldb;
+    t.Bg = We + (size_t)(n * kBN1) * t.ldb;
+    t.Bu = We + (size_t)(P.f + n * kBN1) * t.ldb;
+    t.ktiles = P.d / 64;
+  } else {
+    t.lda = (size_t)P.f * 2;
+    t.ldb = (size_t)P.f * 2;
+    t.A = P.H + (size_t)t.row0 * t.lda;
+    t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * kBN2) * t.ldb;
+    t.Bu = t.Bg + (size_t)64 * t.ldb;
+    t.ktiles = P.f / 64;
+    if (fused) wait_row_ready(P, p);
+  }
+  dispatch_tile<L1>(P, t, lds);
+  if (L1 && fused) publish_row(P, p);
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(GemmParams P) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+  lds_t* lds = (lds_t*)smem;  // address-space cast to the LDS window
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  // Workgroups are dealt round-robin to the 8 XCDs: make consecutive logical
+  // ids share an XCD so a row band's tiles (same A rows) share one L2.
+  const int lid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int Pb = P.meta[META_P];
+  switch (P.mode) {
+    case MODE_SEP_L1:
+      for (int i = lid; i < Pb * P.N1; i += G) do_tile<true>(P, i / P.N1, i % P.N1, false, lds);
+      break;
+    case MODE_SEP_L2:
+      for (int i = lid; i < Pb * P.N2; i += G) do_tile<false>(P, i / P.N2, i % P.N2, false, lds);
+      break;
+    case MODE_WAVE: {
+      const int nw = P.meta[META_NWAVES];
+      for (int wv = 0; wv < nw; ++wv) {
+        const int pb0 = P.wave_band0[wv], pb1 = P.wave_band0[wv + 1];
+        for (int i = lid; i < (pb1 - pb0) * P.N1; i += G) do_tile<true>(P, pb0 + i / P.N1, i % P.N1, true, lds);
+        for (int i = lid; i < (pb1 - pb0) * P.N2; i += G) do_tile<false>(P, pb0 + i / P.N2, i % P.N2, true, lds);
+      }
+      break;
+    }
+    default: {  // MODE_INTERLEAVED
+      const int g = lid >> 1, r = lid & 1, Gp = G >> 1;
+      const int P1 = (P.N1 + 1) >> 1, P2 = (P.N2 + 1) >> 1;
+      const int end1 = Pb * P1, end2 = Pb * P2;
+      int k1 = g, k2 = g;
+      while (k1 < end1 || k2 < end2) {
+        const int p1 = k1 < end1 ? k1 / P1 : 0x3FFFFFFF;
+        const int p2 = k2 / P2;
+        if (k2 < end2 && p2 + P.lead_D <= p1) {
+          const int n = 2 * (k2 % P2) + r;
+          if (n < P.N2) do_tile<false>(P, p2, n, true, lds);
+          k2 += Gp;
+        } else {
+          const int n = 2 * (k1 % P1) + r;
+          if (n < P.N1) do_tile<true>(P, p1, n, true, lds);
+          k1 += Gp;
+        }
+      }
+      break;
+    }
+  }
+}
+
+// Row bands from the per-expert offsets, zeroed l2_full counters, and the
+// expert waves (fewest consecutive experts whose Linear-1 tiles reach the grid,
+// or a fixed number of experts per wave).
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int N1, int G,
+                                                    int wave_experts, int Pmax, int32_t* __restrict__ band_expert,
+                                                    int32_t* __restrict__ band_row0,
+                                                    int32_t* __restrict__ band_rows, int32_t* __restrict__ l2_full,
+                                                    int32_t* __restrict__ wave_band0, int32_t* __restrict__ meta) {
+  __shared__ int start[1025];
+  __shared__ int sh[64];
+  for (int i = threadIdx.x; i < Pmax; i += blockDim.x) l2_full[i] = 0;
+  if (threadIdx.x == 0) meta[META_ERR] = 0;  // the flag reports this call only
+  const int e = threadIdx.x;
+  int cnt = 0, nb = 0;
+  if (e < El) {
+    cnt = offsets[e + 1] - offsets[e];
+    nb = (cnt + kBM - 1) / kBM;
+  }
+  // block exclusive scan of nb
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = nb;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int s = 0;
+    for (int i = 0; i < 16; ++i) { const int v = sh[i]; sh[i] = s; s += v; }
+    sh[16] = s;
+  }
+  __syncthreads();
+  const int first = sh[wv] + x - nb;
+  if (e < El) {
+    start[e] = first;
+    const int r0 = offsets[e];
+    for (int i = 0; i < nb; ++i) {
+      band_expert[first + i] = e;
+      band_row0[first + i] = r0 + i * kBM;
+      band_rows[first + i] = min(kBM, cnt - i * kBM);
+    }
+  }
+  if (threadIdx.x == 0) start[El] = sh[16];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int Ptot = start[El];
+    meta[META_P] = Ptot;
+    meta[META_A] = offsets[El];
+    int nw = 0, tiles = 0, e0 = 0;
+    wave_band0[0] = 0;
+    for (int ex = 0; ex < El; ++ex) {
+      tiles += (start[ex + 1] - start[ex]) * N1;
+      const bool close = wave_experts > 0 ? (ex + 1 - e0 >= wave_experts) : (tiles >= G);
+      if (close || ex == El - 1) {
+        wave_band0[++nw] = start[ex + 1];
+        tiles = 0;
+        e0 = ex + 1;
+      }
+    }
+    meta[META_NWAVES] = nw;
+  }
+}
+
+}  // namespace
+
+int gemm_grid(const moe_problem_t& p) {
+  static thread_local int cached_dev = -1;
+  static thread_local int cached_grid = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(moe_gemm_kernel),
+                                                     kGemmThreads, 0) != hipSuccess)
+      return 0;
+    cached_grid = prop.multiProcessorCount * (occ > 0 ? occ : 1);
+    cached_dev = dev;
+  }
+  int g = cached_grid;
+  if (p.grid > 0 && p.grid < g) g = p.grid;  // never above the co-resident limit
+  if (g > 1 && (g & 1)) --g;                  // pair instances need an even grid
+  return g;
+}
+
+hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
+                                 const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
+                                 const void* W1, const float* W1_scale, const void* W2,
+                                 const float* W2_scale, float* combine_buf, hipStream_t s) {
+  (void)X_perm_scale;
+  (void)W1_scale;
+  (void)W2_scale;
+  const int G = gemm_grid(p);
+  if (G <= 0) return hipErrorInvalidDevice;
+  GemmParams P{};
+  P.X = static_cast<const uint8_t*>(X_perm);
+  P.W1 = static_cast<const uint8_t*>(W1);
+  P.W2 = static_cast<const uint8_t*>(W2);
+  P.H = reinterpret_cast<uint8_t*>(ws + L.pub.h);
+  P.C = combine_buf;
+  P.row_dst = row_dst;
+  P.band_expert = reinterpret_cast<const int32_t*>(ws + L.band_expert);
+  P.band_row0 = reinterpret_cast<const int32_t*>(ws + L.band_row0);
+  P.band_rows = reinterpret_cast<const int32_t*>(ws + L.band_rows);
+  P.l2_full = reinterpret_cast<int32_t*>(ws + L.l2_full);
+  P.meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
+  P.wave_band0 = reinterpret_cast<const int32_t*>(ws + L.wave_band0);
+  P.d = p.d;
+  P.f = p.f;
+  P.N1 = p.f / kBN1;
+  P.N2 = p.d / kBN2;
+  // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
+  // rows of a Linear-1 tile (128), K the participating workgroups and h = f,
+  // i.e. the rows one sweep of the grid covers; at least 1.
+  int D = p.lead_D;
+  if (D <= 0) D = (G + P.N1 - 1) / P.N1;
+  if (D < 1) D = 1;
+  P.lead_D = D;
+
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, L.Pmax,
+                     reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
+                     reinterpret_cast<int32_t*>(ws + L.band_rows), P.l2_full,
+                     reinterpret_cast<int32_t*>(ws + L.wave_band0), P.meta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.sched == MOE_SCHED_SEPARATE) {
+    P.mode = MODE_SEP_L1;
+    hipLaunchKernelGGL(moe_gemm_kernel, dim3(G), dim3(kGemmThreads), 0, s, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    P.mode = MODE_SEP_L2;
+    hipLaunchKernelGGL(moe_gemm_kernel, dim3(G), dim3(kGemmThreads), 0, s, P);
+  } else {
+    P.mode = p.sched == MOE_SCHED_EXPERT_WAVE ? MODE_WAVE : MODE_INTERLEAVED;
+    hipLaunchKernelGGL(moe_gemm_kernel, dim3(G), dim3(kGemmThreads), 0, s, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

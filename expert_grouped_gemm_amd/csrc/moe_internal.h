@@ -1,0 +1,131 @@
+// Internal declarations of the MI355X MoE library: workspace layout, tile
+// constants and the kernel launchers each .hip file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_mi355x.h"
+
+namespace moe {
+
+// Grouped-GEMM tiling (bf16 and fp8 share the byte layout of a stage: 128
+// bytes of K per row, i.e. 64 bf16 or 128 e4m3 values).
+constexpr int kBM = 256;          // rows per row band (scheduler row)
+constexpr int kBN1 = 64;          // SwiGLU output columns per Linear-1 tile (64 gate + 64 up W1 rows)
+constexpr int kBN2 = 128;         // output columns per Linear-2 tile
+constexpr int kBNW = 128;         // weight rows per tile
+constexpr int kKBytes = 128;      // K bytes per row per pipeline stage
+constexpr int kGemmThreads = 256; // 4 wavefronts
+constexpr int kStages = 3;
+constexpr int kStageA = kBM * kKBytes;          // 32 KiB
+constexpr int kStageB = kBNW * kKBytes;         // 16 KiB
+constexpr int kStageBytes = kStageA + kStageB;  // 48 KiB
+constexpr int kGemmLds = kStages * kStageBytes; // 144 KiB of the 160 KiB per CU
+
+constexpr int kMetaInts = 64;
+enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3 };
+
+enum GemmMode { MODE_SEP_L1 = 0, MODE_SEP_L2 = 1, MODE_WAVE = 2, MODE_INTERLEAVED = 3 };
+
+// Spin limit of a Linear-2 tile waiting for its row's Linear-1 tiles (each
+// probe sleeps ~0.05 us plus one memory round trip): well under a second.
+constexpr int kSpinLimit = 1 << 19;
+
+struct Layout {
+  moe_workspace_layout_t pub;
+  // internal
+  size_t blk_counts;   // int32 [nblk, E_l]
+  size_t band_expert;  // int32 [Pmax]
+  size_t band_row0;    // int32 [Pmax]
+  size_t band_rows;    // int32 [Pmax]
+  size_t l2_full;      // int32 [Pmax]
+  size_t wave_band0;   // int32 [E_l + 1]
+  int cap, E_l, nblk, chunk, Pmax;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int dispatch_chunk(int64_t Tk) {
+  // one wavefront per chunk of assignments; at most 1024 chunks
+  int64_t per = (Tk + 1023) / 1024;
+  per = (per + 63) / 64 * 64;
+  if (per < 256) per = 256;
+  return (int)per;
+}
+
+inline Layout make_layout(const moe_problem_t& p) {
+  Layout L{};
+  const int El = p.e_end - p.e_begin;
+  const int64_t cap = (int64_t)p.T * (p.k < El ? p.k : El);
+  const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const size_t esz = fp8 ? 1 : 2;
+  L.cap = (int)cap;
+  L.E_l = El;
+  L.chunk = dispatch_chunk((int64_t)p.T * p.k);
+  L.nblk = (int)(((int64_t)p.T * p.k + L.chunk - 1) / L.chunk);
+  L.Pmax = (int)((cap + kBM - 1) / kBM) + El;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.pub.meta = take(kMetaInts * 4);
+  L.blk_counts = take((size_t)L.nblk * El * 4);
+  L.band_expert = take((size_t)L.Pmax * 4);
+  L.band_row0 = take((size_t)L.Pmax * 4);
+  L.band_rows = take((size_t)L.Pmax * 4);
+  L.l2_full = take((size_t)L.Pmax * 4);
+  L.wave_band0 = take((size_t)(El + 1) * 4);
+  L.pub.topk_idx = take((size_t)p.T * p.k * 4);
+  L.pub.topk_w = take((size_t)p.T * p.k * 4);
+  L.pub.counts = take((size_t)El * 4);
+  L.pub.offsets = take((size_t)(El + 1) * 4);
+  L.pub.row_src = take(cap * 4);
+  L.pub.row_dst = take(cap * 4);
+  L.pub.tok_off = take((size_t)(p.T + 1) * 4);
+  L.pub.comb_w = take(cap * 4);
+  L.pub.x_perm = take(cap * p.d * esz);
+  L.pub.x_perm_scale = take(fp8 ? cap * (p.d / 128) * 4 : 0);
+  L.pub.h = take(cap * p.f * esz);
+  L.pub.h_scale = take(fp8 ? cap * (p.f / 128) * 4 : 0);
+  L.pub.combine_buf = take(cap * p.d * 4);
+  L.pub.total = o;
+  return L;
+}
+
+// Launchers (each returns the first HIP error, hipSuccess otherwise).
+hipError_t launch_route(const moe_problem_t& p, const float* logits, int32_t* idx, float* w,
+                        int32_t* counts_global, hipStream_t s);
+
+hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, const void* X,
+                           const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,
+                           int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                           float* comb_w, void* X_perm, float* X_perm_scale, hipStream_t s);
+
+hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
+                                 const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
+                                 const void* W1, const float* W1_scale, const void* W2,
+                                 const float* W2_scale, float* combine_buf, hipStream_t s);
+
+hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
+                          const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
+
+// Persistent-grid size for the grouped GEMM on the current device.
+int gemm_grid(const moe_problem_t& p);
+
+// Shared device helpers -------------------------------------------------------
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;  // NaN stays NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Output row of token t with S destination segments.
+__host__ __device__ __forceinline__ int y_row_of_token(int t, int T, int S) {
+  return (t % S) * (T / S) + t / S;
+}
+
+}  // namespace moe

@@ -1,0 +1,198 @@
+/*
+ * moe_mi355x.h -- C ABI of one GPU's share of a Mixture-of-Experts layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Cui et al., "Fine-grained Computation-Communication Overlap via
+ * Tile-level Signaling and Scheduling for MoE", Section 2.1; Xian et al.,
+ * "X-Stage: An Overlooked Pipeline Stage for Communication-Computation
+ * Overlap in DiT Inference", Section 2.2 "MegaMoE Execution"):
+ *
+ *   route    : per token, the k largest router logits (descending, ties to
+ *              the lower expert index) and gate weights = softmax over those
+ *              k logits;
+ *   dispatch : the assignments whose expert lies in this GPU's share
+ *              [e_begin, e_end) are permuted into expert-contiguous rows
+ *              (ascending assignment id a = t*k + j inside an expert);
+ *   experts  : per row, h = W1[e] x (2f outputs), act = silu(h[0:f]) * h[f:2f],
+ *              act rounded to the Linear-2 operand type, o = W2[e] act;
+ *   combine  : Y[q(t)] = sum over the token's local slots j (ascending) of
+ *              w[t,j] * o[t,j], accumulated in fp32 and rounded once to bf16;
+ *              tokens with no local expert get 0. With S destination segments
+ *              token t is written to row q(t) = (t mod S) * (T/S) + t div S
+ *              (S contiguous segments of T/S rows), otherwise q(t) = t.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, row-major, densely packed. The library never allocates or
+ *     frees memory: intermediates live in a caller-provided workspace of at
+ *     least moe_workspace_size(p) bytes (256-byte aligned).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream). Returning MOE_OK means "enqueued", not "finished".
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no output is touched.
+ *   - A failed HIP launch returns MOE_ERR_HIP; moe_last_hip_error() gives the
+ *     hipError_t of that failure (per host thread).
+ *   - Calls on one stream are ordered; calls that share a workspace must not
+ *     overlap in time (same or different streams).
+ *   - Router logits must be finite; NaN logits give unspecified routing.
+ *
+ * Shape limits (MOE_ERR_UNSUPPORTED otherwise): 1 <= k <= min(16, E_global),
+ * E_global <= 1024, 0 <= e_begin < e_end <= E_global, T >= 1, T % S == 0,
+ * d % 128 == 0, f % 128 == 0 (fp8 also T % 128 == 0 and
+ * quant_block == 128).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad enum, inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = 2,        /* shape outside the limits above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4,                /* a HIP runtime call failed */
+  MOE_ERR_DEADLOCK = 5            /* a persistent-pipeline wait timed out (reported by moe_check_workspace) */
+} moe_status_t;
+
+typedef enum {
+  MOE_DTYPE_BF16 = 0,             /* X, W1, W2 bfloat16; H bfloat16 */
+  MOE_DTYPE_FP8_E4M3 = 1          /* X, W1, W2 OCP E4M3FN codes with fp32 block scales; H e4m3 with
+                                     one fp32 scale per row and 128 columns */
+} moe_dtype_t;
+
+/* Tile schedule of the grouped expert GEMMs (X-Stage, Section 4.2 "MegaMoE:
+ * Capacity-Aware Scheduling across Expert Waves", Algorithm 1 and Figure 4). */
+typedef enum {
+  MOE_SCHED_SEPARATE = 0,         /* one persistent launch for every Linear-1 tile, then one for every
+                                     Linear-2 tile (stream order is the only dependency) */
+  MOE_SCHED_EXPERT_WAVE = 1,      /* one persistent launch; local experts grouped into waves; a wave's
+                                     Linear-1 tiles, then its Linear-2 tiles, then the next wave */
+  MOE_SCHED_INTERLEAVED = 2       /* one persistent launch; Linear-1 and Linear-2 tile streams merged:
+                                     a Linear-2 tile of row p2 is taken only when the Linear-1 cursor
+                                     leads by at least lead_D rows, otherwise a Linear-1 tile */
+} moe_sched_t;
+
+enum {
+  MOE_FLAG_NONE = 0u
+};
+
+typedef struct moe_problem {
+  int32_t T;             /* tokens */
+  int32_t d;             /* hidden size */
+  int32_t f;             /* expert intermediate size (W1 has 2f rows: gate [0,f), up [f,2f)) */
+  int32_t E_global;      /* experts the router chooses from */
+  int32_t k;             /* experts per token */
+  int32_t e_begin;       /* this GPU's experts: [e_begin, e_end); E_l = e_end - e_begin */
+  int32_t e_end;
+  int32_t dtype;         /* moe_dtype_t */
+  int32_t quant_block;   /* fp8 block edge (128); ignored for bf16 */
+  int32_t num_segments;  /* S >= 1: destination segments of the output rows */
+  int32_t sched;         /* moe_sched_t */
+  int32_t lead_D;        /* interleaved: minimum row lead of Linear-1 over Linear-2 (>= 1);
+                            0 = the anti-starvation knee of X-Stage Eq. 16 */
+  int32_t wave_experts;  /* expert-wave: experts per wave; 0 = fewest experts whose Linear-1
+                            tiles fill the persistent grid */
+  int32_t grid;          /* persistent workgroups; 0 = one per compute unit */
+  uint32_t flags;        /* MOE_FLAG_* (none defined yet; must be 0) */
+} moe_problem_t;
+
+/* Byte offsets of the intermediates inside a workspace (for inspection by
+ * tests and callers; moe_layer_forward writes all of them). cap = T * min(k, E_l). */
+typedef struct moe_workspace_layout {
+  size_t topk_idx;      /* int32 [T, k]                                     */
+  size_t topk_w;        /* fp32  [T, k]                                     */
+  size_t counts;        /* int32 [E_l]      local assignments per expert     */
+  size_t offsets;       /* int32 [E_l + 1]  exclusive prefix sum of counts   */
+  size_t row_src;       /* int32 [cap]      assignment id of expert-ordered row r */
+  size_t row_dst;       /* int32 [cap]      token-order slot of expert-ordered row r */
+  size_t tok_off;       /* int32 [T + 1]    first token-order slot of output row q */
+  size_t comb_w;        /* fp32  [cap]      gate weight of token-order slot p */
+  size_t x_perm;        /* elem  [cap, d]   gathered rows (bf16, or e4m3 codes) */
+  size_t x_perm_scale;  /* fp32  [d/128, cap] fp8 only: scale of row r, column block c at c*cap + r */
+  size_t h;             /* elem  [cap, f]   SwiGLU output (bf16, or e4m3 codes) */
+  size_t h_scale;       /* fp32  [f/128, cap] fp8 only */
+  size_t combine_buf;   /* fp32  [cap, d]   Linear-2 output in token-order slots */
+  size_t meta;          /* int32 [64]       meta[0] = A (local assignments), meta[1] = row bands,
+                                            meta[2] = error flag of the last call (1 = wait timed out) */
+  size_t total;         /* = moe_workspace_size */
+} moe_workspace_layout_t;
+
+/* Workspace bytes for any entry point below (0 if the problem is invalid). */
+MOE_API size_t moe_workspace_size(const moe_problem_t* p);
+
+/* Fills *out with the workspace layout of problem p. */
+MOE_API moe_status_t moe_workspace_get_layout(const moe_problem_t* p, moe_workspace_layout_t* out);
+
+/* Top-k router (Cui et al. Section 2.1 step (1)).
+ *   logits        fp32 [T, E_global]
+ *   topk_idx      int32 [T, k]   out: selected global expert ids, slot order
+ *   topk_w        fp32 [T, k]    out: gate weights (sum to 1 per token)
+ *   counts_global int32 [E_global] out, may be NULL: assignments per global expert (sum T*k) */
+MOE_API moe_status_t moe_route_topk(const moe_problem_t* p, const float* logits, int32_t* topk_idx,
+                                    float* topk_w, int32_t* counts_global, void* stream);
+
+/* Dispatch to this GPU's experts (Cui et al. Section 2.1 step (2), as an
+ * on-GPU permutation). Inputs: X [T, d] (bf16, or e4m3 codes with X_scale
+ * fp32 [T/128, d/128]; X_scale must be NULL for bf16), topk_idx, topk_w.
+ * Outputs: counts, offsets, row_src, row_dst, tok_off, comb_w (see the
+ * layout struct for shapes), X_perm [cap, d] (row r = X row of token
+ * row_src[r] / k) and, for fp8, X_perm_scale [d/128, cap]. Rows >= A of the
+ * cap-sized outputs are left untouched. */
+MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const float* X_scale,
+                                  const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                                  float* comb_w, void* X_perm, float* X_perm_scale, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
+/* Grouped expert FFN over the expert-contiguous rows (X-Stage Section 2.2;
+ * schedule per p->sched). W1 [E_l, 2f, d], W2 [E_l, d, f] (bf16, or e4m3 codes
+ * with W1_scale fp32 [E_l, 2f/128, d/128], W2_scale fp32 [E_l, d/128, f/128]).
+ * Writes combine_buf fp32 [cap, d]: row row_dst[r] = W2[e] act(r). The
+ * intermediate H lives in the workspace. offsets/row_dst as from moe_dispatch. */
+MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
+                                        const int32_t* offsets, const int32_t* row_dst, const void* W1,
+                                        const float* W1_scale, const void* W2, const float* W2_scale,
+                                        float* combine_buf, void* workspace, size_t ws_bytes, void* stream);
+
+/* Weighted combine (Cui et al. Section 2.1 step (5)): Y bf16 [T, d] in
+ * output-row order q; Y_fp32 [T, d] (may be NULL) gets the same sums before
+ * the bf16 rounding. Deterministic: fixed slot order, no atomics. */
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const float* combine_buf, const int32_t* tok_off,
+                                 const float* comb_w, void* Y, float* Y_fp32, void* stream);
+
+/* The whole share: route -> dispatch -> experts -> combine on one stream,
+ * with row counts kept on the device (no host synchronisation). Every
+ * intermediate is left in the workspace at moe_workspace_get_layout's offsets. */
+MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
+                                       const float* logits, const void* W1, const float* W1_scale,
+                                       const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
+                                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Synchronises `stream` and reads the workspace's error flag, which every
+ * moe_expert_forward / moe_layer_forward call clears when it starts:
+ * MOE_ERR_DEADLOCK if a persistent-pipeline wait of the most recent call on
+ * this workspace timed out (its outputs are then invalid). Clears the flag. */
+MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace, size_t ws_bytes,
+                                         void* stream);
+
+MOE_API const char* moe_status_string(moe_status_t s);
+MOE_API int moe_last_hip_error(void);
+/* Library version, e.g. "0.1.0". */
+MOE_API const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

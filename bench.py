@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the MoE layer on MI355X.
+
+A step is one pass of the whole share (route -> dispatch -> grouped expert
+GEMMs -> combine) over one batch of synthetic inputs already resident in HBM,
+issued as the four C-ABI calls moe_route_topk, moe_dispatch,
+moe_expert_forward and moe_combine (the same kernels moe_layer_forward runs)
+with HIP events between them on the launch stream, so every stage is timed
+live inside the timed region.
+
+Default workload: the DeepSeek-style share (T=4096 tokens, d=7168, f=2048,
+top-8 of 256 experts, this GPU owns experts 0-31, bf16). Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--sched interleaved|expert_wave|separate]
+                  [--no-cpu-baseline] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="deepseek_share_bf16")
+    ap.add_argument("--sched", default="interleaved", choices=["interleaved", "expert_wave", "separate"])
+    ap.add_argument("--lead-D", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 1 GiB device copy (HBM reference and counter calibration)")
+    return ap.parse_args()
+
+
+def gemm_bytes(cfg, counts) -> float:
+    """Algorithmic HBM bytes of one grouped-GEMM launch (Linear-1 + SwiGLU +
+    Linear-2): each local expert with at least one row streams its W1 and W2
+    once; per row: X_perm read (d), H write and read (2f), combine-buffer
+    write (4d bytes)."""
+    esz = 1 if cfg.dtype == "fp8_e4m3" else 2
+    active = sum(1 for c in counts if c > 0)
+    A = sum(counts)
+    w = active * 3 * cfg.f * cfg.d * esz
+    rows = A * (cfg.d * esz + 2 * cfg.f * esz + 4 * cfg.d)
+    return float(w + rows)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's share of the layer; --gpus {args.gpus} is not supported on this "
+              f"single-GPU build (the multi-GPU split is expert parallelism, documented, not run)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_grouped_gemm_amd as moe
+    import moe_synth
+
+    cfg = moe_synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    fp8 = cfg.dtype == "fp8_e4m3"
+
+    g = moe_synth.generate(cfg, device=dev)
+    torch.cuda.synchronize()
+    p = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
+                         num_segments=cfg.num_segments, sched=args.sched, lead_D=args.lead_D,
+                         quant_block=cfg.quant_block)
+    ws = moe.alloc_workspace(p)
+    v = moe.workspace_views(p, ws)
+    Y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.route_topk(p, g["logits"], v["topk_idx"], v["topk_w"], None, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.dispatch(p, g["X"], g.get("X_scale"), v["topk_idx"], v["topk_w"], v["counts"], v["offsets"],
+                     v["row_src"], v["row_dst"], v["tok_off"], v["comb_w"], v["x_perm"], v.get("x_perm_scale"),
+                     ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.expert_forward(p, v["x_perm"], v.get("x_perm_scale"), v["offsets"], v["row_dst"], g["W1"],
+                           g.get("W1_scale"), g["W2"], g.get("W2_scale"), v["combine_buf"], ws, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.combine(p, v["combine_buf"], v["tok_off"], v["comb_w"], Y, None, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.check_workspace(p, ws)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moe.check_workspace(p, ws)
+
+    stage_names = ["route", "dispatch", "expert_gemm", "combine"]
+    per = {n: [events[i][j].elapsed_time(events[i][j + 1]) * 1e3 for i in range(args.steps)]
+           for j, n in enumerate(stage_names)}
+    med = {n: statistics.median(x) for n, x in per.items()}
+
+    counts = v["counts"].cpu().tolist()
+    A = int(sum(counts))
+    ms_per_step = wall * 1e3 / args.steps
+    useful_flop = 6.0 * A * cfg.d * cfg.f
+    tflops = useful_flop / (ms_per_step * 1e-3) / 1e12
+    peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+
+    esz = 1 if fp8 else 2
+    gb = gemm_bytes(cfg, counts)
+    gemm_us = statistics.mean(per["expert_gemm"])
+    achieved = gb / (gemm_us * 1e-6) / 1e9
+    disp_bytes = 2.0 * A * cfg.d * esz + cfg.T * cfg.k * 8.0
+    comb_bytes = A * cfg.d * 4.0 + cfg.T * cfg.d * 2.0
+    out = {
+        "metric": "fused MoE-layer useful TFLOP/s (6*A*d*f per step); % of MFMA peak; dispatch/combine GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) weights, drawn on the GPU)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E_global": cfg.E_global,
+                   "k": cfg.k, "local_experts": [cfg.e_begin, cfg.e_end], "segments": cfg.num_segments,
+                   "sched": args.sched, "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "stages_us_median": {n: round(x, 2) for n, x in med.items()},
+        "dispatch_GBps": round(disp_bytes / (med["dispatch"] * 1e-6) / 1e9, 1),
+        "combine_GBps": round(comb_bytes / (med["combine"] * 1e-6) / 1e9, 1),
+        "roofline": {
+            "kernel": "moe_gemm_kernel (grouped Linear-1+SwiGLU+Linear-2, one persistent launch)"
+            if args.sched != "separate" else "moe_gemm_kernel (Linear-1 launch + Linear-2 launch)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gb,
+            "avg_launch_us": round(gemm_us, 2),
+        },
+    }
+
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        out["copy_probe"] = {"bytes_moved": 2 * n, "us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1)}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, g, args)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, g, args):
+    """The oracle (fp64 NumPy) as it stands, timed on this host on a bounded
+    sample: full routing and dispatch of all T tokens plus the expert FFNs and
+    combine of the first n tokens' local assignments. Rate = useful FLOP of the
+    sampled assignments / wall time."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    n = args.cpu_sample_tokens or min(cfg.T, 256)
+    host = {k: t.cpu() for k, t in g.items()}
+    tokens = np.arange(n)
+    t0 = time.perf_counter()
+    r = oracle.moe_layer(host, cfg, tokens=tokens)
+    dt = time.perf_counter() - t0
+    t_of = r["row_src"] // cfg.k
+    A_s = int(np.sum(t_of < n))
+    flop = 6.0 * A_s * cfg.d * cfg.f
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens ({A_s} local assignments; routing+dispatch of all tokens), "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -74,48 +74,47 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ tok_off,
                                                              int32_t* __restrict__ meta) {
   __shared__ int sh[64];
-  // per-expert totals and per-chunk exclusive bases (thread e owns expert e)
+  // per-expert totals and per-chunk exclusive bases (thread e owns expert e;
+  // at most 64 chunks, independent loads)
   const int e = threadIdx.x;
   int tot = 0;
   if (e < El) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_counts[(size_t)b * El + e];
-      blk_counts[(size_t)b * El + e] = tot;
-      tot += c;
-    }
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) tot += blk_counts[(size_t)b * El + e];
   }
   int A;
   const int off = block_exclusive_scan_1024(e < El ? tot : 0, sh, &A);
   if (e < El) {
     counts[e] = tot;
     offsets[e] = off;
-    for (int b = 0; b < nblk; ++b) blk_counts[(size_t)b * El + e] += off;
+    int run = off;
+#pragma unroll 8
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_counts[(size_t)b * El + e];
+      blk_counts[(size_t)b * El + e] = run;
+      run += c;
+    }
   }
   if (e == 0) {
     offsets[El] = A;
     meta[META_A] = A;
   }
-  // per-output-row local counts, scanned in row order q
-  const int per = (T + 1023) / 1024;
-  const int q0 = threadIdx.x * per;
+  // output rows in blocks of 1024: q -> token t, local slots of t, block scan
   const int seg = T / S;
-  int run = 0;
-  for (int q = q0; q < min(T, q0 + per); ++q) {
-    const int t = (q % seg) * S + q / seg;
-    int c = 0;
-    for (int j = 0; j < k; ++j) c += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
-    run += c;
+  int base = 0;
+  for (int q0 = 0; q0 < T; q0 += 1024) {
+    const int q = q0 + threadIdx.x;
+    int cnt = 0;
+    if (q < T) {
+      const int t = (q % seg) * S + q / seg;
+      for (int j = 0; j < k; ++j) cnt += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
+    }
+    int blk_total;
+    const int x = block_exclusive_scan_1024(cnt, sh, &blk_total);
+    if (q < T) tok_off[q] = base + x;
+    base += blk_total;
   }
-  int total;
-  int base = block_exclusive_scan_1024(run, sh, &total);
-  for (int q = q0; q < min(T, q0 + per); ++q) {
-    const int t = (q % seg) * S + q / seg;
-    tok_off[q] = base;
-    int c = 0;
-    for (int j = 0; j < k; ++j) c += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
-    base += c;
-  }
-  if (threadIdx.x == 0) tok_off[T] = total;
+  if (threadIdx.x == 0) tok_off[T] = base;
 }
 
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
@@ -133,7 +132,6 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
   const int Tk = T * k;
   const int a0 = blockIdx.x * chunk;
   const int a1 = min(Tk, a0 + chunk);
-  const int seg = T / S;
   for (int g = a0; g < a1; g += 64) {
     const int a = g + lane;
     const int e = (a < a1) ? idx[a] - e_begin : -1;
@@ -164,7 +162,6 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
       comb_w[slot] = w[a];
     }
   }
-  (void)seg;
 }
 
 // X_perm[r, :] = X[row_src[r] / k, :] for r < A; fp8 also gathers the row's

@@ -82,6 +82,14 @@ struct Tile {
   int ktiles;             // K / 64
 };
 
+// LDS ring geometry per number of 32-row blocks MB: a stage holds MB*32 rows
+// of the band plus the 128 weight rows, 128 bytes of K each.
+__host__ __device__ constexpr int stage_a_bytes(int MB) { return MB * 32 * kKBytes; }
+__host__ __device__ constexpr int stage_bytes(int MB) { return stage_a_bytes(MB) + kBNW * kKBytes; }
+__host__ __device__ constexpr int ring_stages(int MB) {
+  return kGemmLds / stage_bytes(MB) > 8 ? 8 : kGemmLds / stage_bytes(MB);
+}
+
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * kKBytes + ((chunk ^ (row & 7)) << 4); }
 
 // Workgroup barrier that orders LDS accesses only. __syncthreads() would also
@@ -118,14 +126,15 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st) {
     const int r = r0 + sub;
     const uint8_t* base = r < 64 ? t.Bg : t.Bu;
     const uint8_t* g = base + (size_t)(r & 63) * t.ldb + kb + ((slot ^ (r & 7)) << 4);
-    __builtin_amdgcn_global_load_lds(g, st + kStageA + r0 * kKBytes, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB) + r0 * kKBytes, 16, 0, 0);
   }
 }
 
 // MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
 // and weight rows {nb*64 + wn*32 .. +32} for nb = 0, 1.
 template <int NMB>
-__device__ __forceinline__ void compute_stage(const lds_t* st, int wm, int wn, f32x16 (&acc)[NMB][2]) {
+__device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, int wm, int wn,
+                                              f32x16 (&acc)[NMB][2]) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -134,11 +143,11 @@ __device__ __forceinline__ void compute_stage(const lds_t* st, int wm, int wn, f
     bf16x8 b[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      b[nb] = *(const lds_bf16x8*)(st + kStageA + lds_off(nb * 64 + wn * 32 + lr, chunk));
+      b[nb] = *(const lds_bf16x8*)(sb + lds_off(nb * 64 + wn * 32 + lr, chunk));
 #pragma unroll
     for (int mi = 0; mi < NMB; ++mi) {
       const int row = (wm + 2 * mi) * 32 + lr;
-      const bf16x8 a = *(const lds_bf16x8*)(st + lds_off(row, chunk));
+      const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off(row, chunk));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mi][nb], 0, 0, 0);
@@ -178,11 +187,25 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
   }
 }
 
+// Drain the last R+1 stages of the ring: stage rd is complete once at most
+// R stages (R * (MB + 4) loads per lane) are still in flight.
+template <int MB, int NMB, int R>
+__device__ __forceinline__ void drain(lds_t* lds, int rd, int wm, int wn, f32x16 (&acc)[NMB > 0 ? NMB : 1][2]) {
+  constexpr int S = ring_stages(MB), SB = stage_bytes(MB);
+  wait_vmcnt<R * (MB + 4)>();
+  lds_barrier();
+  if constexpr (NMB > 0) compute_stage<NMB>(lds + rd * SB, lds + rd * SB + stage_a_bytes(MB), wm, wn, acc);
+  if constexpr (R > 0) drain<MB, NMB, R - 1>(lds, rd + 1 == S ? 0 : rd + 1, wm, wn, acc);
+}
+
 // The whole tile for one wavefront role: every wavefront runs the same number
 // of loads and barriers; NMB (its share of the MB row blocks) only changes the
 // MFMA and epilogue work, and the accumulators stay inside this function.
+// The LDS ring has ring_stages(MB) stages of stage_bytes(MB): as many as fit
+// in 160 KiB, so that S-1 stages of weight bytes are in flight per CU.
 template <int MB, int NMB, bool L1>
 __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds, int wm, int wn) {
+  constexpr int S = ring_stages(MB), SB = stage_bytes(MB), SA = stage_a_bytes(MB);
   f32x16 acc[NMB > 0 ? NMB : 1][2];
 #pragma unroll
   for (int a = 0; a < (NMB > 0 ? NMB : 1); ++a)
@@ -191,30 +214,29 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  // K >= 128 bytes * 2 stages is guaranteed by the shape checks (d, f % 128 == 0).
   const int KT = t.ktiles;
-  lds_t* s0 = lds;
-  lds_t* s1 = lds + kStageBytes;
-  lds_t* s2 = lds + 2 * kStageBytes;
-  issue_stage<MB>(t, 0, s0);
-  issue_stage<MB>(t, 1, s1);
-  for (int kt = 0; kt + 2 < KT; ++kt) {
-    wait_vmcnt<MB + 4>();    // this lane's loads of stage kt have landed
-    lds_barrier();           // ... everyone's; and stage kt-1 (in s2) is no longer read
-    issue_stage<MB>(t, kt + 2, s2);
-    if constexpr (NMB > 0) compute_stage<NMB>(s0, wm, wn, acc);
-    lds_t* r = s0;
-    s0 = s1;
-    s1 = s2;
-    s2 = r;
+  if (KT < S) {
+    // the whole K extent fits in the ring
+    for (int kt = 0; kt < KT; ++kt) issue_stage<MB>(t, kt, lds + kt * SB);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if constexpr (NMB > 0)
+      for (int kt = 0; kt < KT; ++kt) compute_stage<NMB>(lds + kt * SB, lds + kt * SB + SA, wm, wn, acc);
+  } else {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue_stage<MB>(t, s, lds + s * SB);
+    int rd = 0, wr = S - 1;
+    for (int kt = 0; kt + S - 1 < KT; ++kt) {
+      wait_vmcnt<(S - 2) * (MB + 4)>();  // this lane's loads of stage kt have landed
+      lds_barrier();                     // ... everyone's; and slot wr (stage kt-1) is no longer read
+      issue_stage<MB>(t, kt + S - 1, lds + wr * SB);
+      if constexpr (NMB > 0) compute_stage<NMB>(lds + rd * SB, lds + rd * SB + SA, wm, wn, acc);
+      rd = rd + 1 == S ? 0 : rd + 1;
+      wr = wr + 1 == S ? 0 : wr + 1;
+    }
+    drain<MB, NMB, S - 2>(lds, rd, wm, wn, acc);
   }
-  wait_vmcnt<MB + 4>();
-  lds_barrier();
-  if constexpr (NMB > 0) compute_stage<NMB>(s0, wm, wn, acc);
-  wait_vmcnt<0>();
-  lds_barrier();
-  if constexpr (NMB > 0) compute_stage<NMB>(s1, wm, wn, acc);
-  __syncthreads();  // LDS ring free for the next tile
+  lds_barrier();  // LDS ring free for the next tile
   if constexpr (NMB > 0) epilogue<NMB, L1>(P, t, wm, wn, acc);
 }
 

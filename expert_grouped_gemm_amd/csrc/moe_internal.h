@@ -18,11 +18,7 @@ constexpr int kBN2 = 128;         // output columns per Linear-2 tile
 constexpr int kBNW = 128;         // weight rows per tile
 constexpr int kKBytes = 128;      // K bytes per row per pipeline stage
 constexpr int kGemmThreads = 256; // 4 wavefronts
-constexpr int kStages = 3;
-constexpr int kStageA = kBM * kKBytes;          // 32 KiB
-constexpr int kStageB = kBNW * kKBytes;         // 16 KiB
-constexpr int kStageBytes = kStageA + kStageB;  // 48 KiB
-constexpr int kGemmLds = kStages * kStageBytes; // 144 KiB of the 160 KiB per CU
+constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
 constexpr int kMetaInts = 64;
 enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3 };
@@ -48,8 +44,8 @@ struct Layout {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int dispatch_chunk(int64_t Tk) {
-  // one wavefront per chunk of assignments; at most 1024 chunks
-  int64_t per = (Tk + 1023) / 1024;
+  // one wavefront per chunk of assignments; at most 64 chunks
+  int64_t per = (Tk + 63) / 64;
   per = (per + 63) / 64 * 64;
   if (per < 256) per = 256;
   return (int)per;

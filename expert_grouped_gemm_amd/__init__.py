@@ -52,7 +52,7 @@ class Problem(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_idx", "topk_w", "counts", "offsets", "row_src", "row_dst", "tok_off", "comb_w", "x_perm",
-        "x_perm_scale", "h", "h_scale", "combine_buf", "meta", "total")]
+        "x_perm_scale", "h", "h_scale", "h_f32", "combine_buf", "meta", "total")]
 
 
 _lib = None
@@ -171,6 +171,7 @@ def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
     if esz == 1:
         v["x_perm_scale"] = view(L.x_perm_scale, cap * (p.d // 128), torch.float32, (p.d // 128, cap))
         v["h_scale"] = view(L.h_scale, cap * (p.f // 128), torch.float32, (p.f // 128, cap))
+        v["h_f32"] = view(L.h_f32, cap * p.f, torch.float32, (cap, p.f))
     return v
 
 

@@ -32,7 +32,6 @@ moe_status_t check_problem(const moe_problem_t* p) {
     return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_DTYPE_FP8_E4M3) {
     if (p->quant_block != 128 || p->f % 128 || p->T % 128) return MOE_ERR_UNSUPPORTED;
-    return MOE_ERR_UNSUPPORTED;  // the fp8 expert kernels are not built yet
   }
   return MOE_OK;
 }

@@ -84,6 +84,7 @@ inline Layout make_layout(const moe_problem_t& p) {
   L.pub.h = take(cap * p.f * esz);
   L.pub.h_scale = take(fp8 ? cap * (p.f / 128) * 4 : 0);
   L.pub.combine_buf = take(cap * p.d * 4);
+  L.pub.h_f32 = take(fp8 ? cap * p.f * 4 : 0);
   L.pub.total = o;
   return L;
 }

@@ -123,6 +123,7 @@ typedef struct moe_workspace_layout {
   size_t x_perm_scale;  /* fp32  [d/128, cap] fp8 only: scale of row r, column block c at c*cap + r */
   size_t h;             /* elem  [cap, f]   SwiGLU output (bf16, or e4m3 codes) */
   size_t h_scale;       /* fp32  [f/128, cap] fp8 only */
+  size_t h_f32;         /* fp32  [cap, f]   fp8 only: SwiGLU output before its e4m3 quantisation */
   size_t combine_buf;   /* fp32  [cap, d]   Linear-2 output in token-order slots */
   size_t meta;          /* int32 [64]       meta[0] = A (local assignments), meta[1] = row bands,
                                             meta[2] = error flag of the last call (1 = wait timed out) */

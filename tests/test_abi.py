@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(moe.Problem) == 15 * 4
-    assert ctypes.sizeof(moe.WorkspaceLayout) == 15 * 8
+    assert ctypes.sizeof(moe.WorkspaceLayout) == 16 * 8
 
 
 GOOD = dict(T=64, d=128, f=256, E_global=4, k=2)

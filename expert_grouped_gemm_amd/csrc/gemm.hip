@@ -364,10 +364,21 @@ __device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t
   }
 }
 
+// Wait until row band p's H is complete. Thread 0 polls l2_full[p] with
+// device-scope loads (they bypass the CU's L1 and see the value the
+// producers' device-scope atomics left), then the workgroup proceeds.
+//
+// No cache invalidation is needed before the H loads: a band's H lines are
+// first read only after the band is complete (only Linear-2 tiles of band p
+// read them, and only after this wait), rows are whole multiples of 128-byte
+// lines so no line is shared by two bands, and every launch starts with the
+// kernel-entry acquire; so neither this CU's L1 nor its XCD's L2 can hold a
+// stale copy. Invalidating the L2 here would instead discard the weight and
+// activation lines the other 31 CUs of the XCD are reusing.
 __device__ __forceinline__ void wait_row_ready(const GemmParams& P, int p) {
   if (threadIdx.x == 0) {
     int spins = 0;
-    while (__hip_atomic_load(&P.l2_full[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < P.ready) {
+    while (__hip_atomic_load(&P.l2_full[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P.ready) {
       // after one timeout in this call every later wait gives up at once
       if (__hip_atomic_load(&P.meta[META_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
       __builtin_amdgcn_s_sleep(2);
@@ -378,7 +389,21 @@ __device__ __forceinline__ void wait_row_ready(const GemmParams& P, int p) {
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Make this workgroup's global stores visible at device scope, then let
+// thread 0 add `inc` to l2_full[p]: every wave waits for its own stores to be
+// acknowledged (vmcnt(0)), the barrier orders that before thread 0, whose
+// device-scope release writes the XCD's L2 back before the increment.
+__device__ __forceinline__ int publish(const GemmParams& P, int p, int inc) {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __syncthreads();
+  int old = 0;
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    old = __hip_atomic_fetch_add(&P.l2_full[p], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return old;
 }
 
 // fp8: per row, per 128 columns of the band's fp32 SwiGLU output, scale =
@@ -411,24 +436,20 @@ __device__ void quantize_band(const GemmParams& P, int row0, int rows) {
 // H and then bumps the counter once more, to N1 + 1.
 template <bool FP8>
 __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& t, int p, bool fused, lds_t* lds) {
-  if (!FP8 && !fused) return;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
   if constexpr (!FP8) {
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(&P.l2_full[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (fused) publish(P, p, 1);
   } else {
     __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)lds;
-    if (threadIdx.x == 0)
-      *flag = __hip_atomic_fetch_add(&P.l2_full[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = publish(P, p, 1);
+    if (threadIdx.x == 0) *flag = old;
     __syncthreads();
     const bool last = *flag == P.N1 - 1;
     __syncthreads();  // the ring (and the flag in it) is reused by the next tile
     if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // every other tile of the band has published its Hf stores; this
+      // workgroup reads those lines for the first time (no stale copies)
       quantize_band(P, t.row0, t.rows);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(&P.l2_full[p], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      publish(P, p, 1);
     }
   }
 }
@@ -646,10 +667,14 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.ready = fp8 ? P.N1 + 1 : P.N1;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile (128), K the participating workgroups and h = f,
-  // i.e. the rows one sweep of the grid covers; at least 1.
+  // i.e. the rows one sweep of the grid covers. The knee is a lower bound;
+  // below 8 rows Linear-2 tiles were measured to spin on the Mixtral shape
+  // (f = 14336: knee 2), so the default lead is max(knee, 8).
   int D = p.lead_D;
-  if (D <= 0) D = (G + P.N1 - 1) / P.N1;
-  if (D < 1) D = 1;
+  if (D <= 0) {
+    D = (G + P.N1 - 1) / P.N1;
+    if (D < 8) D = 8;
+  }
   P.lead_D = D;
 
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, L.Pmax,

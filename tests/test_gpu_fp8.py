@@ -87,3 +87,20 @@ def test_fp8_schedule_invariance_bitwise():
     for kw in (dict(sched="expert_wave"), dict(sched="interleaved"), dict(sched="interleaved", lead_D=1, grid=8)):
         Y, _, _ = run_layer(problem_of(cfg, **kw), g, want_fp32=False)
         assert torch.equal(Y.view(torch.int16), base.view(torch.int16)), kw
+
+
+def test_fp8_fused_schedules_never_read_stale_h():
+    """As for bf16: poisoned workspace (0xFF: e4m3 NaN codes, NaN fp32 staging)
+    before every fused call; Y must equal the separate-launch Y bit for bit."""
+    import expert_grouped_gemm_amd as moe
+    cfg = FP8["fp8_small_segments"]
+    g = to_gpu(moe_synth.generate(cfg))
+    base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
+    for kw in (dict(sched="interleaved"), dict(sched="interleaved", lead_D=1), dict(sched="expert_wave")):
+        p = problem_of(cfg, **kw)
+        ws = moe.alloc_workspace(p)
+        for _ in range(3):
+            ws.fill_(0xFF)
+            Y, _, _ = run_layer(p, g, ws=ws, want_fp32=False)
+            moe.check_workspace(p, ws)
+            assert torch.equal(Y.view(torch.int16), base.view(torch.int16)), kw

@@ -167,3 +167,24 @@ def test_repeat_runs_deterministic_and_no_stale_state():
     Y1, _, _ = run_layer(p, g, ws=ws, want_fp32=False)
     Y2, _, _ = run_layer(p, g, ws=ws, want_fp32=False)
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["ragged_share", "multi_band", "zipf_small"])
+def test_fused_schedules_never_read_stale_h(name):
+    """The fused schedules read H only after its row band is published. With
+    the whole workspace poisoned (0xFF bytes: NaN in bf16) before every call,
+    any read of H before its band is complete would leak NaN into Y; the
+    result must equal the separate-launch result bit for bit, call after call."""
+    import expert_grouped_gemm_amd as moe
+    cfg = SMALL[name]
+    g = to_gpu(moe_synth.generate(cfg))
+    base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
+    for kw in (dict(sched="interleaved"), dict(sched="interleaved", lead_D=1), dict(sched="expert_wave"),
+               dict(sched="interleaved", grid=16)):
+        p = problem_of(cfg, **kw)
+        ws = moe.alloc_workspace(p)
+        for _ in range(3):
+            ws.fill_(0xFF)
+            Y, _, _ = run_layer(p, g, ws=ws, want_fp32=False)
+            moe.check_workspace(p, ws)
+            assert torch.equal(Y.view(torch.int16), base.view(torch.int16)), kw

@@ -75,13 +75,14 @@ struct GemmParams {
   const int32_t* band_row0;
   const int32_t* band_rows;
   int32_t* l2_full;
+  int32_t* blk_done;      // fp8: [Pmax, f/128] Linear-1 tiles stored per (band, 128-column block)
   int32_t* meta;
   const int32_t* wave_band0;
   int d, f;
   int N1, N2;             // Linear-1 tiles per row band (f / 64), Linear-2 tiles (d / 128)
   int mode;
   int lead_D;
-  int ready;              // l2_full value at which a row band's H is complete (N1, or N1 + 1 with fp8)
+  int ready;              // l2_full value at which a row band's H is complete (N1, or f/128 with fp8)
 };
 
 struct Tile {
@@ -242,11 +243,21 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
   }
 }
 
+// Load p[i] where p and i are the same in every lane, through the scalar
+// cache (a read-only weight scale): a vector load here would be counted by
+// vmcnt and force a wait that drains the global->LDS prefetch ring.
+__device__ __forceinline__ float uniform_load(const float* p, int i) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p + i);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *reinterpret_cast<const __attribute__((address_space(4))) float*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int MB, int NMB, bool FP8>
 __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int wm, int wn,
                                             f32x16 (&acc)[NMB][2]) {
   if constexpr (FP8) {
-    const float swg = t.Sg[kt], swu = t.Su[kt];
+    const float swg = uniform_load(t.Sg, kt), swu = uniform_load(t.Su, kt);
     compute_stage_fp8<NMB>(st, st + stage_a_bytes(MB), st + stage_a_bytes(MB) + stage_b_bytes(), swg, swu, wm,
                            wn, acc);
   } else {
@@ -392,16 +403,17 @@ __device__ __forceinline__ void wait_row_ready(const GemmParams& P, int p) {
 }
 
 // Make this workgroup's global stores visible at device scope, then let
-// thread 0 add `inc` to l2_full[p]: every wave waits for its own stores to be
+// thread 0 add `inc` to a readiness counter (returned: its old value, in
+// thread 0): every wave waits for its own stores to be
 // acknowledged (vmcnt(0)), the barrier orders that before thread 0, whose
 // device-scope release writes the XCD's L2 back before the increment.
-__device__ __forceinline__ int publish(const GemmParams& P, int p, int inc) {
+__device__ __forceinline__ int publish(int32_t* counter, int inc) {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
   __syncthreads();
   int old = 0;
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    old = __hip_atomic_fetch_add(&P.l2_full[p], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return old;
 }
@@ -430,26 +442,64 @@ __device__ void quantize_band(const GemmParams& P, int row0, int rows) {
   }
 }
 
-// After a Linear-1 tile's stores: count it in l2_full[p]. bf16: that is the
-// readiness signal (only the fused schedules read it). fp8: the tile that
-// completes the band (the counter's old value is N1 - 1) quantises the band's
-// H and then bumps the counter once more, to N1 + 1.
+// fp8: quantise column block j (128 SwiGLU columns) of a row band: per row,
+// scale = amax / 448 (1 for an all-zero block) and code = e4m3(value /
+// scale), round to nearest even. 16 lanes per row (8 values each), 16 rows per
+// pass; the loads of four passes are issued before any is used.
+__device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
+  const int rr = threadIdx.x >> 4, q = threadIdx.x & 15;
+  const int col = j * 128 + q * 8;
+  for (int base = 0; base < rows; base += 64) {
+    float4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = base + u * 16 + rr;
+      if (r < rows) {
+        const float4* src = reinterpret_cast<const float4*>(P.Hf + (size_t)(row0 + r) * P.f + col);
+        v[u][0] = src[0];
+        v[u][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = base + u * 16 + rr;
+      if (r >= rows) continue;  // uniform across the 16 lanes of a row
+      const float4 a = v[u][0], b = v[u][1];
+      float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                         fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+      const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a.x / scale, a.y / scale, 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(a.z / scale, a.w / scale, lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b.x / scale, b.y / scale, 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(b.z / scale, b.w / scale, hi, true);
+      *reinterpret_cast<uint2*>(P.H + (size_t)(row0 + r) * P.f + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
+      if (q == 0) P.Hs[(size_t)j * P.cap + row0 + r] = scale;
+    }
+  }
+}
+
+// After a Linear-1 tile's stores. bf16 (fused schedules only): count the tile
+// in l2_full[p]; the band is ready at N1. fp8: tiles 2j and 2j+1 cover column
+// block j; each counts itself in blk_done[p][j], and the second of the two
+// (old value 1; every one of the block's Hf stores is then published)
+// quantises the block and counts it in l2_full[p]; the band is ready at N1/2.
 template <bool FP8>
 __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& t, int p, bool fused, lds_t* lds) {
   if constexpr (!FP8) {
-    if (fused) publish(P, p, 1);
+    if (fused) publish(P.l2_full + p, 1);
   } else {
+    const int j = t.n >> 1;
     __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)lds;
-    const int old = publish(P, p, 1);
+    const int old = publish(P.blk_done + (size_t)p * (P.f >> 7) + j, 1);
     if (threadIdx.x == 0) *flag = old;
     __syncthreads();
-    const bool last = *flag == P.N1 - 1;
+    const bool second = *flag == 1;
     __syncthreads();  // the ring (and the flag in it) is reused by the next tile
-    if (last) {
-      // every other tile of the band has published its Hf stores; this
-      // workgroup reads those lines for the first time (no stale copies)
-      quantize_band(P, t.row0, t.rows);
-      publish(P, p, 1);
+    if (second) {
+      quantize_block(P, t.row0, t.rows, j);
+      publish(P.l2_full + p, 1);
     }
   }
 }
@@ -550,13 +600,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(GemmParams P)
 // expert waves (fewest consecutive experts whose Linear-1 tiles reach the grid,
 // or a fixed number of experts per wave).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int N1, int G,
-                                                    int wave_experts, int Pmax, int32_t* __restrict__ band_expert,
+                                                    int wave_experts, int Pmax, int32_t* __restrict__ blk_done,
+                                                    int nblk_done, int32_t* __restrict__ band_expert,
                                                     int32_t* __restrict__ band_row0,
                                                     int32_t* __restrict__ band_rows, int32_t* __restrict__ l2_full,
                                                     int32_t* __restrict__ wave_band0, int32_t* __restrict__ meta) {
   __shared__ int start[1025];
   __shared__ int sh[64];
   for (int i = threadIdx.x; i < Pmax; i += blockDim.x) l2_full[i] = 0;
+  for (int i = threadIdx.x; i < nblk_done; i += blockDim.x) blk_done[i] = 0;
   if (threadIdx.x == 0) meta[META_ERR] = 0;  // the flag reports this call only
   const int e = threadIdx.x;
   int cnt = 0, nb = 0;
@@ -664,7 +716,8 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.f = p.f;
   P.N1 = p.f / kBN1;
   P.N2 = p.d / kBN2;
-  P.ready = fp8 ? P.N1 + 1 : P.N1;
+  P.ready = fp8 ? p.f / 128 : P.N1;
+  P.blk_done = reinterpret_cast<int32_t*>(ws + L.blk_done);
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile (128), K the participating workgroups and h = f,
   // i.e. the rows one sweep of the grid covers. The knee is a lower bound;
@@ -678,7 +731,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.lead_D = D;
 
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, L.Pmax,
-                     reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
+                     P.blk_done, fp8 ? L.Pmax * (p.f / 128) : 0, reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
                      reinterpret_cast<int32_t*>(ws + L.band_rows), P.l2_full,
                      reinterpret_cast<int32_t*>(ws + L.wave_band0), P.meta);
   hipError_t e = hipGetLastError();

@@ -38,6 +38,7 @@ struct Layout {
   size_t band_rows;    // int32 [Pmax]
   size_t l2_full;      // int32 [Pmax]
   size_t wave_band0;   // int32 [E_l + 1]
+  size_t blk_done;     // int32 [Pmax, f/128] (fp8 only)
   int cap, E_l, nblk, chunk, Pmax;
 };
 
@@ -71,6 +72,7 @@ inline Layout make_layout(const moe_problem_t& p) {
   L.band_rows = take((size_t)L.Pmax * 4);
   L.l2_full = take((size_t)L.Pmax * 4);
   L.wave_band0 = take((size_t)(El + 1) * 4);
+  L.blk_done = take(fp8 ? (size_t)L.Pmax * (p.f / 128) * 4 : 0);
   L.pub.topk_idx = take((size_t)p.T * p.k * 4);
   L.pub.topk_w = take((size_t)p.T * p.k * 4);
   L.pub.counts = take((size_t)El * 4);

@@ -59,6 +59,27 @@ def gemm_bytes(cfg, counts) -> float:
     return float(w + rows)
 
 
+def measured_traffic(cfg, sched):
+    """HBM bytes per grouped-GEMM launch measured with rocprofv3 FETCH_SIZE /
+    WRITE_SIZE (scaled by a plain-copy calibration) for this workload and
+    schedule, as recorded in profiles/gemm_traffic_<workload>_<sched>.md; null
+    when no record exists or the GEMM source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{cfg.name}_{sched}.md")
+    src = os.path.join(ROOT, "expert_grouped_gemm_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    text = open(path).read()
+    try:
+        blob = json.loads(text.split("```json")[1].split("```")[0])
+    except (IndexError, ValueError):
+        return None
+    if blob.get("gemm_source_sha256_16") != digest:
+        return None
+    return blob.get("hbm_bytes_per_launch")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,7 +157,14 @@ def main():
     esz = 1 if fp8 else 2
     gb = gemm_bytes(cfg, counts)
     gemm_us = statistics.mean(per["expert_gemm"])
-    achieved = gb / (gemm_us * 1e-6) / 1e9
+    # The grouped GEMM is bound by HBM when its arithmetic intensity (useful
+    # FLOP per algorithmic byte) is below the ridge point peak_flops / 8 TB/s.
+    intensity = useful_flop / gb
+    ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if intensity < ridge:
+        bound, achieved, rpeak, runit = "hbm", gb / (gemm_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, achieved, rpeak, runit = "mfma", useful_flop / (gemm_us * 1e-6) / 1e12, peak, "TFLOP/s"
     disp_bytes = 2.0 * A * cfg.d * esz + cfg.T * cfg.k * 8.0
     comb_bytes = A * cfg.d * 4.0 + cfg.T * cfg.d * 2.0
     out = {
@@ -162,13 +190,15 @@ def main():
         "roofline": {
             "kernel": "moe_gemm_kernel (grouped Linear-1+SwiGLU+Linear-2, one persistent launch)"
             if args.sched != "separate" else "moe_gemm_kernel (Linear-1 launch + Linear-2 launch)",
-            "bound": "hbm",
+            "bound": bound,
             "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "peak": rpeak,
+            "unit": runit,
+            "frac": round(achieved / rpeak, 4),
+            "traffic": measured_traffic(cfg, args.sched),
             "algorithmic_bytes_per_launch": gb,
+            "useful_flop_per_launch": useful_flop,
+            "arithmetic_intensity_flop_per_byte": round(intensity, 1),
             "avg_launch_us": round(gemm_us, 2),
         },
     }
@@ -196,9 +226,10 @@ def main():
 
 def cpu_baseline(cfg, g, args):
     """The oracle (fp64 NumPy) as it stands, timed on this host on a bounded
-    sample: full routing and dispatch of all T tokens plus the expert FFNs and
-    combine of the first n tokens' local assignments. Rate = useful FLOP of the
-    sampled assignments / wall time."""
+    sample: routing and dispatch of all T tokens plus the expert FFNs and the
+    combine of the first n tokens' local assignments, n doubling from 256
+    until one run takes at least 10 s (or covers every token). Rate = useful
+    FLOP of the sampled assignments / wall time of that run."""
     import numpy as np
     import oracle
     try:
@@ -206,14 +237,17 @@ def cpu_baseline(cfg, g, args):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    n = args.cpu_sample_tokens or min(cfg.T, 256)
     host = {k: t.cpu() for k, t in g.items()}
-    tokens = np.arange(n)
-    t0 = time.perf_counter()
-    r = oracle.moe_layer(host, cfg, tokens=tokens)
-    dt = time.perf_counter() - t0
-    t_of = r["row_src"] // cfg.k
-    A_s = int(np.sum(t_of < n))
+    n = args.cpu_sample_tokens or 256
+    while True:
+        n = min(n, cfg.T)
+        t0 = time.perf_counter()
+        r = oracle.moe_layer(host, cfg, tokens=np.arange(n))
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or n >= cfg.T or args.cpu_sample_tokens:
+            break
+        n *= 2
+    A_s = int(np.sum(r["row_src"] // cfg.k < n))
     flop = 6.0 * A_s * cfg.d * cfg.f
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens ({A_s} local assignments; routing+dispatch of all tokens), "

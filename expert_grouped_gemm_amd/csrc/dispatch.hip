@@ -7,9 +7,9 @@
 // Assignment a = t*k + j is local when topk_idx[a] lies in [e_begin, e_end).
 // Rows of one expert are ordered by ascending a (a stable counting sort), so
 // the permutation is unique and needs no atomics:
-//   1. count   : one wavefront per chunk of assignments, LDS histogram of
-//                local experts -> blk_counts[chunk][e]
-//   2. scan    : one block; per-expert totals, offsets, per-chunk bases;
+//   1. count   : one wavefront per chunk of assignments (at most 512 chunks),
+//                LDS histogram of local experts -> blk_counts[e][chunk]
+//   2. scan    : one block; per-expert chunk prefixes, totals, offsets;
 //                per-output-row local counts -> tok_off (exclusive scan)
 //   3. scatter : one wavefront per chunk, walking its assignments in order;
 //                the rank of an assignment among equal experts in a group of
@@ -21,20 +21,37 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t* __restrict__ idx, int Tk, int chunk,
-                                                            int e_begin, int El,
-                                                            int32_t* __restrict__ blk_counts) {
-  extern __shared__ int32_t hist[];
-  for (int e = threadIdx.x; e < El; e += 64) hist[e] = 0;
+// Chunk b holds assignments [b*chunk, (b+1)*chunk); one wavefront per chunk,
+// four chunks per 256-thread block, a private LDS histogram per wavefront.
+// blk_counts is expert-major, [E_l][nblk], so that the scan's per-expert
+// prefix reads contiguous memory.
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                             int S, int chunk, int e_begin, int El, int nblk,
+                                                             int32_t* __restrict__ blk_counts,
+                                                             int32_t* __restrict__ tok_cnt) {
+  const int Tk = T * k;
+  extern __shared__ int32_t hist_all[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + w;
+  int32_t* hist = hist_all + w * El;
+  for (int e = lane; e < El; e += 64) hist[e] = 0;
   __syncthreads();
-  const int a0 = blockIdx.x * chunk;
-  const int a1 = min(Tk, a0 + chunk);
-  for (int a = a0 + threadIdx.x; a < a1; a += 64) {
-    const int e = idx[a] - e_begin;
-    if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
+  if (b < nblk) {
+    const int a0 = b * chunk, a1 = min(Tk, a0 + chunk);
+    for (int a = a0 + lane; a < a1; a += 64) {
+      const int e = idx[a] - e_begin;
+      if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
+    }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < El; e += 64) blk_counts[(size_t)blockIdx.x * El + e] = hist[e];
+  if (b < nblk)
+    for (int e = lane; e < El; e += 64) blk_counts[(size_t)e * nblk + b] = hist[e];
+  // local slots of each token, stored at its output row q
+  for (int t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
+    tok_cnt[y_row_of_token(t, T, S)] = c;
+  }
 }
 
 // Exclusive scan over a 1024-thread block; returns the exclusive prefix of v
@@ -66,75 +83,116 @@ __device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ idx, int T, int k,
-                                                             int S, int e_begin, int El, int nblk,
+// One block. (1) Per expert (one wavefront per expert, eight chunks per lane
+// loaded together): exclusive prefix of its chunk counts, in place, and the
+// expert total. (2) offsets = exclusive scan of the totals; A. (3) tok_off:
+// exclusive scan of the local-slot counts of the output rows.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tok_cnt, int T, int El,
+                                                             int nblk,
                                                              int32_t* __restrict__ blk_counts,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ tok_off,
                                                              int32_t* __restrict__ meta) {
   __shared__ int sh[64];
-  // per-expert totals and per-chunk exclusive bases (thread e owns expert e;
-  // at most 64 chunks, independent loads)
-  const int e = threadIdx.x;
-  int tot = 0;
-  if (e < El) {
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) tot += blk_counts[(size_t)b * El + e];
-  }
-  int A;
-  const int off = block_exclusive_scan_1024(e < El ? tot : 0, sh, &A);
-  if (e < El) {
-    counts[e] = tot;
-    offsets[e] = off;
-    int run = off;
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_counts[(size_t)b * El + e];
-      blk_counts[(size_t)b * El + e] = run;
-      run += c;
+  __shared__ int tot[1024];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int e = w; e < El; e += 16) {
+    int run = 0;
+    for (int g0 = 0; g0 < nblk; g0 += 512) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = g0 + u * 64 + lane;
+        v[u] = b < nblk ? blk_counts[(size_t)e * nblk + b] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int x = v[u];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        const int b = g0 + u * 64 + lane;
+        if (b < nblk) blk_counts[(size_t)e * nblk + b] = run + x - v[u];
+        run += __shfl(x, 63, 64);
+      }
     }
+    if (lane == 0) tot[e] = run;
+  }
+  __syncthreads();
+  int A;
+  const int e = threadIdx.x;
+  const int off = block_exclusive_scan_1024(e < El ? tot[e] : 0, sh, &A);
+  if (e < El) {
+    counts[e] = tot[e];
+    offsets[e] = off;
   }
   if (e == 0) {
     offsets[El] = A;
     meta[META_A] = A;
   }
-  // output rows in blocks of 1024: q -> token t, local slots of t, block scan
-  const int seg = T / S;
-  int base = 0;
-  for (int q0 = 0; q0 < T; q0 += 1024) {
-    const int q = q0 + threadIdx.x;
-    int cnt = 0;
-    if (q < T) {
-      const int t = (q % seg) * S + q / seg;
-      for (int j = 0; j < k; ++j) cnt += (unsigned)(idx[(size_t)t * k + j] - e_begin) < (unsigned)El;
-    }
-    int blk_total;
-    const int x = block_exclusive_scan_1024(cnt, sh, &blk_total);
-    if (q < T) tok_off[q] = base + x;
-    base += blk_total;
+  // output rows: wavefront w owns a contiguous segment of q and reads it
+  // 64 consecutive rows at a time (coalesced); segment totals are scanned
+  // across the 16 wavefronts in LDS.
+  const int segw = ((T + 15) / 16 + 63) / 64 * 64;
+  const int qa = min(T, w * segw), qb = min(T, qa + segw);
+  int wsum = 0;
+#pragma unroll 4
+  for (int q = qa + lane; q < qb; q += 64) wsum += tok_cnt[q];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+  if (lane == 0) sh[32 + w] = wsum;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int v = sh[32 + i];
+    run += i < w ? v : 0;
+    total += v;
   }
-  if (threadIdx.x == 0) tok_off[T] = base;
+#pragma unroll 4
+  for (int q0 = qa; q0 < qb; q0 += 64) {
+    const int q = q0 + lane;
+    const int c = q < qb ? tok_cnt[q] : 0;
+    int x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (q < qb) tok_off[q] = run + x - c;
+    run += __shfl(x, 63, 64);
+  }
+  if (threadIdx.x == 0) tok_off[T] = total;
 }
 
+// One wavefront per chunk, walking its assignments in order, 64 at a time.
+// A token's k experts are distinct, so within one expert the order is the
+// order of the tokens; the rank of a lane among the lanes of its group that
+// hold the same expert comes from a ballot (a match-any loop), the running
+// base of each expert (offset + chunk prefix) from LDS.
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
                                                               const float* __restrict__ w, int T, int k, int S,
-                                                              int chunk, int e_begin, int El,
-                                                              const int32_t* __restrict__ blk_base,
+                                                              int chunk, int e_begin, int El, int nblk,
+                                                              const int32_t* __restrict__ blk_prefix,
+                                                              const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ tok_off,
                                                               int32_t* __restrict__ row_src,
                                                               int32_t* __restrict__ row_dst,
                                                               float* __restrict__ comb_w) {
   extern __shared__ int32_t running[];
   const int lane = threadIdx.x;
-  for (int e = lane; e < El; e += 64) running[e] = blk_base[(size_t)blockIdx.x * El + e];
+  for (int e = lane; e < El; e += 64) running[e] = offsets[e] + blk_prefix[(size_t)e * nblk + blockIdx.x];
   __syncthreads();
   const int Tk = T * k;
   const int a0 = blockIdx.x * chunk;
   const int a1 = min(Tk, a0 + chunk);
+  int next = (a0 + lane < a1) ? idx[a0 + lane] : 0;
   for (int g = a0; g < a1; g += 64) {
     const int a = g + lane;
-    const int e = (a < a1) ? idx[a] - e_begin : -1;
+    const int e = (a < a1) ? next - e_begin : -1;
+    if (g + 64 < a1) next = (a + 64 < a1) ? idx[a + 64] : 0;  // next group's experts, loaded early
     const bool local = (unsigned)e < (unsigned)El;
     uint64_t pending = __ballot(local);
     int pos = 0;
@@ -143,19 +201,16 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
       const int v = __shfl(e, leader, 64);
       const uint64_t same = __ballot(local && e == v);
       const int base = running[v];
-      if (local && e == v) {
-        const uint64_t below = same & ((1ull << lane) - 1ull);
-        pos = base + __popcll(below);
-      }
-      __syncthreads();
+      if (local && e == v) pos = base + __popcll(same & ((1ull << lane) - 1ull));
       if (lane == leader) running[v] = base + __popcll(same);
-      __syncthreads();
       pending &= ~same;
     }
     if (local) {
       const int t = a / k, j = a - t * k;
       int before = 0;
-      for (int jj = 0; jj < j; ++jj) before += (unsigned)(idx[(size_t)t * k + jj] - e_begin) < (unsigned)El;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+        if (jj < j) before += (unsigned)(idx[(size_t)t * k + jj] - e_begin) < (unsigned)El;
       const int slot = tok_off[y_row_of_token(t, T, S)] + before;
       row_src[pos] = a;
       row_dst[pos] = slot;
@@ -193,19 +248,20 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, co
                            const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,
                            int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
                            float* comb_w, void* X_perm, float* X_perm_scale, hipStream_t s) {
-  const int Tk = p.T * p.k;
   const int El = L.E_l;
   int32_t* blk = reinterpret_cast<int32_t*>(ws + L.blk_counts);
   int32_t* meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nblk), dim3(64), El * 4, s, idx, Tk, L.chunk, p.e_begin, El,
-                     blk);
+  int32_t* tok_cnt = reinterpret_cast<int32_t*>(ws + L.tok_cnt);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3((L.nblk + 3) / 4), dim3(256), 4 * El * 4, s, idx, p.T, p.k,
+                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, tok_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, idx, p.T, p.k, p.num_segments, p.e_begin,
-                     El, L.nblk, blk, counts, offsets, tok_off, meta);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, tok_cnt, p.T, El, L.nblk, blk, counts,
+                     offsets, tok_off, meta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nblk), dim3(64), El * 4, s, idx, w, p.T, p.k,
-                     p.num_segments, L.chunk, p.e_begin, El, blk, tok_off, row_src, row_dst, comb_w);
+                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, offsets, tok_off, row_src, row_dst,
+                     comb_w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
   const int row_bytes = p.d * (fp8 ? 1 : 2);

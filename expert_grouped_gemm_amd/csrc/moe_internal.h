@@ -32,7 +32,8 @@ constexpr int kSpinLimit = 1 << 19;
 struct Layout {
   moe_workspace_layout_t pub;
   // internal
-  size_t blk_counts;   // int32 [nblk, E_l]
+  size_t blk_counts;   // int32 [E_l, nblk]
+  size_t tok_cnt;      // int32 [T] local slots per output row
   size_t band_expert;  // int32 [Pmax]
   size_t band_row0;    // int32 [Pmax]
   size_t band_rows;    // int32 [Pmax]
@@ -44,11 +45,16 @@ struct Layout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline int dispatch_chunk(int64_t Tk) {
-  // one wavefront per chunk of assignments; at most 64 chunks
-  int64_t per = (Tk + 63) / 64;
+// Dispatch chunk size: a multiple of 64 assignments (one wavefront step),
+// as small as possible while the [chunks, E_l] count matrix keeps at most 512
+// chunks and 2^20 entries.
+inline int dispatch_chunk(int64_t Tk, int El) {
+  int64_t nmax = (1 << 20) / (El > 0 ? El : 1);
+  if (nmax > 512) nmax = 512;
+  if (nmax < 1) nmax = 1;
+  int64_t per = (Tk + nmax - 1) / nmax;
   per = (per + 63) / 64 * 64;
-  if (per < 256) per = 256;
+  if (per < 64) per = 64;
   return (int)per;
 }
 
@@ -60,13 +66,14 @@ inline Layout make_layout(const moe_problem_t& p) {
   const size_t esz = fp8 ? 1 : 2;
   L.cap = (int)cap;
   L.E_l = El;
-  L.chunk = dispatch_chunk((int64_t)p.T * p.k);
+  L.chunk = dispatch_chunk((int64_t)p.T * p.k, El);
   L.nblk = (int)(((int64_t)p.T * p.k + L.chunk - 1) / L.chunk);
   L.Pmax = (int)((cap + kBM - 1) / kBM) + El;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.pub.meta = take(kMetaInts * 4);
   L.blk_counts = take((size_t)L.nblk * El * 4);
+  L.tok_cnt = take((size_t)p.T * 4);
   L.band_expert = take((size_t)L.Pmax * 4);
   L.band_row0 = take((size_t)L.Pmax * 4);
   L.band_rows = take((size_t)L.Pmax * 4);

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", default="deepseek_share_bf16")
     ap.add_argument("--sched", default="interleaved", choices=["interleaved", "expert_wave", "separate"])
     ap.add_argument("--lead-D", type=int, default=0)
+    ap.add_argument("--tiles", default="auto", choices=["auto", "narrow", "wide"],
+                    help="expert-GEMM tile width (default: chosen from the shape)")
+    ap.add_argument("--band-major", action="store_true", help="no grouped raster of the GEMM tile lists")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -59,17 +62,28 @@ def gemm_bytes(cfg, counts) -> float:
     return float(w + rows)
 
 
+GEMM_SOURCES = ("gemm_device.h", "gemm.hip", "gemm_bf16.hip", "gemm_fp8.hip")
+
+
+def gemm_source_digest():
+    """First 16 hex digits of the SHA-256 of the expert-GEMM sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "expert_grouped_gemm_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(cfg, sched):
     """HBM bytes per grouped-GEMM launch measured with rocprofv3 FETCH_SIZE /
     WRITE_SIZE (scaled by a plain-copy calibration) for this workload and
     schedule, as recorded in profiles/gemm_traffic_<workload>_<sched>.md; null
     when no record exists or the GEMM source changed since it was taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"gemm_traffic_{cfg.name}_{sched}.md")
-    src = os.path.join(ROOT, "expert_grouped_gemm_amd", "csrc", "gemm.hip")
     if not os.path.exists(path):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    digest = gemm_source_digest()
     text = open(path).read()
     try:
         blob = json.loads(text.split("```json")[1].split("```")[0])
@@ -103,7 +117,7 @@ def main():
     torch.cuda.synchronize()
     p = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
                          num_segments=cfg.num_segments, sched=args.sched, lead_D=args.lead_D,
-                         quant_block=cfg.quant_block)
+                         quant_block=cfg.quant_block, tiles=args.tiles, band_major=args.band_major)
     ws = moe.alloc_workspace(p)
     v = moe.workspace_views(p, ws)
     Y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
@@ -182,7 +196,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) weights, drawn on the GPU)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E_global": cfg.E_global,
                    "k": cfg.k, "local_experts": [cfg.e_begin, cfg.e_end], "segments": cfg.num_segments,
-                   "sched": args.sched, "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
+                   "sched": args.sched, "tiles": args.tiles, "band_major": args.band_major,
+                   "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "stages_us_median": {n: round(x, 2) for n, x in med.items()},
         "dispatch_GBps": round(disp_bytes / (med["dispatch"] * 1e-6) / 1e9, 1),

@@ -29,6 +29,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED", 
           4: "MOE_ERR_HIP", 5: "MOE_ERR_DEADLOCK"}
 SCHED = {"separate": 0, "expert_wave": 1, "interleaved": 2}
 DTYPE = {"bf16": 0, "fp8_e4m3": 1}
+# MOE_FLAG_* of moe_mi355x.h
+TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
+FLAG_BAND_MAJOR = 4
 
 
 class MoEError(RuntimeError):
@@ -95,11 +98,15 @@ def lib() -> ctypes.CDLL:
 
 def make_problem(T: int, d: int, f: int, E_global: int, k: int, e_begin: int = 0, e_end: Optional[int] = None,
                  dtype: str = "bf16", num_segments: int = 1, sched: str = "interleaved", lead_D: int = 0,
-                 wave_experts: int = 0, grid: int = 0, quant_block: int = 128) -> Problem:
+                 wave_experts: int = 0, grid: int = 0, quant_block: int = 128, tiles: str = "auto",
+                 band_major: bool = False) -> Problem:
+    """tiles: "auto" (chosen from the shape), "narrow" or "wide" expert-GEMM tiles;
+    band_major: walk the separate / expert-wave tile lists band by band."""
+    flags = TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0)
     return Problem(T=T, d=d, f=f, E_global=E_global, k=k, e_begin=e_begin,
                    e_end=E_global if e_end is None else e_end, dtype=DTYPE[dtype], quant_block=quant_block,
                    num_segments=num_segments, sched=SCHED[sched], lead_D=lead_D, wave_experts=wave_experts,
-                   grid=grid, flags=0)
+                   grid=grid, flags=flags)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

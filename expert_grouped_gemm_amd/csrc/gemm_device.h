@@ -1,0 +1,662 @@
+// Device side of the persistent grouped expert GEMM with a SwiGLU Linear-1 epilogue and a
+// combine-store Linear-2 epilogue, on gfx950 bf16 MFMA.
+//
+// What it computes (X-Stage: An Overlooked Pipeline Stage for Communication-
+// Computation Overlap in DiT Inference, Section 2.2 "MegaMoE Execution"):
+// per local expert e and expert-contiguous row r of X_perm,
+//   Linear-1 + SwiGLU : H[r, j]  = bf16( silu(W1[e][j] . x_r) * (W1[e][f+j] . x_r) )
+//   Linear-2          : C[row_dst[r], n] = W2[e][n] . H[r]          (fp32)
+//
+// How the work is cut (Cui et al., Section 3.3.1: one rank-wide persistent
+// kernel walks a unified tile list, each item an (expert, tile) pair, with
+// the expert's pointers substituted per item; X-Stage Algorithm 1 for the
+// ordering):
+//   - a row band p is up to kBM = 256 consecutive rows of one expert; bands
+//     are listed expert by expert (row p of the scheduler);
+//   - a tile holds NNB * 64 weight rows, NNB = 2 (narrow) or 4 (wide): a
+//     Linear-1 tile (p, n1) covers NNB * 32 SwiGLU columns, i.e. as many gate
+//     rows and as many up rows of W1[e]; a Linear-2 tile (p, n2) covers
+//     NNB * 64 output columns;
+//   - the K loop streams 128-byte slices of every row through an LDS ring of
+//     as many stages as fit in 160 KiB, filled by direct global->LDS loads
+//     (global_load_lds_dwordx4), so the weight tile is read once per band and
+//     reused by every row of the band;
+//   - 4 wavefronts, 2 (rows) x 2 (columns); a wavefront owns the 32-row
+//     blocks {wm, wm+2, ...} of the band and NNB 32-column blocks, one
+//     v_mfma_f32_32x32x16_bf16 accumulator each; the number of 32-row blocks
+//     (rounded up to even) is a template parameter, so a short band costs
+//     fewer loads and MFMAs;
+//   - in the separate and expert-wave schedules the tile list is walked in
+//     groups of group_m row bands, N-tile by N-tile inside a group, so the
+//     tiles that run at the same time on one XCD share both their row bands
+//     and their weight tiles through that XCD's L2.
+//
+// Schedules (X-Stage Section 4.2, Algorithm 1, Figure 4):
+//   MODE_SEP_L1/L2    every Linear-1 tile, then (next launch) every Linear-2 tile
+//   MODE_WAVE         experts grouped into waves; a wave's Linear-1 tiles, then
+//                     its Linear-2 tiles; each Linear-2 tile waits on l2_full[p]
+//   MODE_INTERLEAVED  per pair-instance g (two workgroups, roles r = 0, 1) two
+//                     cursors k1, k2 advance by the instance count; a Linear-2
+//                     tile of row p2 = k2 / P2 is emitted only when the Linear-1
+//                     row p1 = k1 / P1 leads it by at least D rows, otherwise
+//                     the next Linear-1 tile; the N-tile of a pair cursor is
+//                     n = 2 (k mod P) + r.
+// l2_full[p] counts stored Linear-1 tiles of row p (X-Stage Section 4.2,
+// "Condition 2"): the Linear-1 epilogue publishes with an agent-scope release
+// after its H stores, a Linear-2 tile of row p acquires once it reaches the
+// number of Linear-1 tiles per row. A workgroup only waits on rows at least
+// D >= 1 behind its own Linear-1 cursor, so the smallest unfinished Linear-1
+// row always belongs to a workgroup that is not waiting (no deadlock while
+// the whole grid is resident: one workgroup per CU). Waits are bounded; a
+// timeout sets the sticky error flag meta[META_ERR].
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+struct GemmParams {
+  const uint8_t* X;       // X_perm [cap, d] (bf16 or e4m3 codes)
+  const uint8_t* W1;      // [E_l, 2f, d]
+  const uint8_t* W2;      // [E_l, d, f]
+  uint8_t* H;             // [cap, f] Linear-2 operand (bf16 or e4m3 codes)
+  float* C;               // combine_buf [cap, d]
+  // fp8 only: block scales and the fp32 SwiGLU output before quantisation
+  const float* Xs;        // [d/128, cap]  scale of X_perm row r, K block c at c*cap + r
+  const float* W1s;       // [E_l, 2f/128, d/128]
+  const float* W2s;       // [E_l, d/128, f/128]
+  float* Hs;              // [f/128, cap]
+  float* Hf;              // [cap, f] fp32
+  int cap;
+  const int32_t* row_dst;
+  const int32_t* band_expert;
+  const int32_t* band_row0;
+  const int32_t* band_rows;
+  int32_t* l2_full;
+  int32_t* blk_done;      // fp8: [Pmax, f/128] Linear-1 tiles stored per (band, 128-column block)
+  int32_t* meta;
+  const int32_t* wave_band0;
+  int d, f;
+  int N1, N2;             // Linear-1 tiles per row band (f / (32 nnb1)), Linear-2 tiles (d / (64 nnb2))
+  int nnb1, nnb2;         // tile width (2 or 4) of the Linear-1 and Linear-2 tiles
+  int group_m;            // row bands per raster group (separate and expert-wave schedules)
+  int mode;
+  int lead_D;
+  int ready;              // l2_full value at which a row band's H is complete (N1, or f/128 with fp8)
+};
+
+// Launch the persistent expert-GEMM kernel of one operand type (bf16 in
+// gemm_bf16.hip, fp8 in gemm_fp8.hip: each type is its own translation unit
+// so the two compile in parallel) on G workgroups, and the kernel's address
+// for occupancy queries.
+hipError_t launch_gemm_bf16(const GemmParams& P, int G, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmParams& P, int G, hipStream_t s);
+const void* gemm_kernel_bf16();
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t lds_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+
+struct Tile {
+  const uint8_t* A;       // first row of the band (X_perm or H)
+  const uint8_t* Bg;      // first half of the tile's weight rows (Linear-1: the gate rows)
+  const uint8_t* Bu;      // second half (Linear-1: the matching up rows)
+  size_t lda, ldb;        // row pitch in bytes
+  int rows;               // valid rows of the band (1..256)
+  int row0;               // first X_perm / H row of the band
+  int n;                  // N-tile index
+  int ktiles;             // K bytes / stage_k_bytes
+  // fp8 only
+  const float* As;        // row scales of K block 0 for the band's first row (next block: + cap)
+  const float* Sg;        // weight block scales of the first half along K (one per 128-byte stage)
+  const float* Su;        // weight block scales of the second half
+  int cap_stride;         // elements between consecutive K blocks of the row scales
+};
+
+// K bytes per row per pipeline stage: 64 bf16 values, or for fp8 one 128-wide
+// scale block of e4m3 values. (64-byte bf16 stages, which double the ring
+// depth of a wide tile, were measured no faster on the compute-bound shapes
+// and slower on the bandwidth-bound ones.)
+__host__ __device__ constexpr int stage_k_bytes(bool) { return 128; }
+
+// LDS ring geometry per number of 32-row blocks MB and tile width NNB: a stage
+// holds MB*32 rows of the band plus the NNB*64 weight rows, stage_k_bytes of K
+// each; with fp8 also the 256 row scales of the stage's K block (1 KiB).
+__host__ __device__ constexpr int stage_a_bytes(int MB, bool FP8) { return MB * 32 * stage_k_bytes(FP8); }
+__host__ __device__ constexpr int stage_b_bytes(int NNB, bool FP8) { return NNB * 64 * stage_k_bytes(FP8); }
+__host__ __device__ constexpr int stage_bytes(int MB, int NNB, bool FP8) {
+  return stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + (FP8 ? kBM * 4 : 0);
+}
+__host__ __device__ constexpr int ring_stages(int MB, int NNB, bool FP8) {
+  return kGemmLds / stage_bytes(MB, NNB, FP8) > 8 ? 8 : kGemmLds / stage_bytes(MB, NNB, FP8);
+}
+// global -> LDS loads issued per lane per stage (16 bytes each, plus one
+// 4-byte row-scale load with fp8)
+__host__ __device__ constexpr int stage_loads(int MB, int NNB, bool FP8) {
+  return (MB * 32 + NNB * 64) * stage_k_bytes(FP8) / (kGemmThreads * 16) + (FP8 ? 1 : 0);
+}
+
+// 16-byte chunk c of row `row` in a stage of KB-byte rows. The chunk index is
+// XOR-swizzled so that the 16 consecutive rows a 16-lane phase of
+// ds_read_b128 touches spread over all 64 LDS banks (256 bytes): 128-byte rows
+// pair up in a bank line, so the swizzle is (row / 2) mod 8.
+template <int KB>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  static_assert(KB == 128, "stage row size");
+  return (row >> 1) & 7;
+}
+template <int KB>
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * KB + ((chunk ^ chunk_swizzle<KB>(row)) << 4);
+}
+
+// Workgroup barrier that orders LDS accesses only. __syncthreads() would also
+// drain every outstanding global load (vmcnt(0)), which would empty the
+// prefetch ring; global->LDS completion is tracked explicitly with
+// wait_vmcnt instead.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One pipeline stage: K bytes [kt*KB, kt*KB+KB) of the band's first 32*MB
+// rows and of the tile's NNB*64 weight rows (and, with fp8, the 256 row scales
+// of K block kt), in stage_loads(MB, NNB, FP8) load instructions per lane:
+// first the band rows, then the weight rows, then the scales. Lane i of a
+// 16-byte instruction lands at LDS base + 16*i (64/CH rows of KB bytes, CH =
+// KB/16 chunks per row), lane i of a 4-byte instruction at base + 4*i.
+// issue_load issues instruction j of the stage. (Spreading a stage's loads
+// between the MFMAs of the previous stage, instead of issuing them together,
+// was measured no faster.)
+template <int MB, int NNB, bool FP8>
+__device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
+  constexpr int KB = stage_k_bytes(FP8), CH = KB / 16, RPI = 64 / CH;
+  constexpr int NA = MB * 32 / (4 * RPI), NBW = NNB * 64 / (4 * RPI), half = NNB * 32;
+  const int w = tid >> 6, lane = tid & 63;
+  const int kb = kt * KB;
+  const int sub = lane / CH, slot = lane % CH;
+  if (j < NA) {
+    const int r0 = (j * 4 + w) * RPI;
+    const int r = r0 + sub;
+    const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
+    const uint8_t* g = t.A + (size_t)gr * t.lda + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
+    __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
+  } else if (j < NA + NBW) {
+    const int r0 = ((j - NA) * 4 + w) * RPI;
+    const int r = r0 + sub;
+    const uint8_t* base = r < half ? t.Bg : t.Bu;
+    const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
+    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + r0 * KB, 16, 0, 0);
+  } else if constexpr (FP8) {
+    const int r = w * 64 + lane;
+    const int gr = r < t.rows ? r : t.rows - 1;
+    const float* g = t.As + (size_t)kt * t.cap_stride + gr;
+    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + w * 256, 4, 0, 0);
+  }
+}
+
+template <int MB, int NNB, bool FP8>
+__device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, int tid) {
+#pragma unroll
+  for (int j = 0; j < stage_loads(MB, NNB, FP8); ++j) issue_load<MB, NNB, FP8>(t, kt, st, tid, j);
+}
+
+// MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
+// and weight rows {nb*64 + wn*32 .. +32} for nb = 0 .. NNB-1.
+// The K order inside a stage is a permutation shared by both operands (lane
+// half h of an MFMA reads the same chunk indices of its A row and B row), so
+// the sum over K is unchanged.
+template <int NMB, int NNB>
+__device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, int tid, f32x16 (&acc)[NMB][NNB]) {
+  constexpr int KB = stage_k_bytes(false);
+  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < KB / 32; ++ks) {
+    const int chunk = ks * 2 + hi;
+    bf16x8 b[NNB];
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+      b[nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(nb * 64 + wn * 32 + lr, chunk));
+#pragma unroll
+    for (int mi = 0; mi < NMB; ++mi) {
+      const int row = (wm + 2 * mi) * 32 + lr;
+      const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off<KB>(row, chunk));
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mi][nb], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ i32x8 lds_read_32B(const lds_t* base, int row, int chunk0) {
+  const i32x4 lo = *(const lds_i32x4*)(base + lds_off<128>(row, chunk0));
+  const i32x4 hi = *(const lds_i32x4*)(base + lds_off<128>(row, chunk0 + 1));
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// fp8 stage: the stage is exactly one 128-wide K block, so the block's MFMA
+// sum (two v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales) is
+// promoted into the fp32 accumulator with the row's activation scale times
+// the weight block's scale: acc += partial * sx[row] * sw, with sw = swg for
+// the first half of the weight rows and swu for the second.
+template <int NMB, int NNB>
+__device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* sb, const lds_t* ss, float swg,
+                                                  float swu, int tid, f32x16 (&acc)[NMB][NNB]) {
+  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+  const int lr = lane & 31, hi = lane >> 5;
+  i32x8 b[2][NNB];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) b[ks][nb] = lds_read_32B(sb, nb * 64 + wn * 32 + lr, ks * 4 + hi * 2);
+  const f32x16 zero = {};
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    const int mb = wm + 2 * mi;
+    f32x16 part[NNB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i32x8 a = lds_read_32B(sa, mb * 32 + lr, ks * 4 + hi * 2);
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[ks][nb], ks ? part[nb] : zero, 0, 0, 0,
+                                                                   127, 0, 127);
+    }
+    // the lane's rows of block mb: mb*32 + 8*g + 4*hi + (0..3), g = 0..3
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 sx = *(const lds_f32x4*)(ss + (mb * 32 + 8 * g + 4 * hi) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb)
+          acc[mi][nb][i] = fmaf(part[nb][i], sx[j] * (nb < NNB / 2 ? swg : swu), acc[mi][nb][i]);
+      }
+    }
+  }
+}
+
+// Load p[i] where p and i are the same in every lane, through the scalar
+// cache (a read-only weight scale): a vector load here would be counted by
+// vmcnt and force a wait that drains the global->LDS prefetch ring.
+__device__ __forceinline__ float uniform_load(const float* p, int i) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p + i);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *reinterpret_cast<const __attribute__((address_space(4))) float*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int MB, int NMB, int NNB, bool FP8>
+__device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int tid,
+                                            f32x16 (&acc)[NMB][NNB]) {
+  if constexpr (FP8) {
+    const float swg = uniform_load(t.Sg, kt), swu = uniform_load(t.Su, kt);
+    static_assert(stage_k_bytes(true) == 128, "an fp8 stage is one 128-wide scale block");
+    compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8),
+                                swg, swu, tid, acc);
+  } else {
+    compute_stage<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), tid, acc);
+  }
+}
+
+// Accumulator element i of a 32x32 block sits at row 8*(i/4) + 4*(lane/32) + i%4,
+// column lane%32.
+template <int NMB, int NNB, bool L1, bool FP8>
+__device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
+                                         const f32x16 (&acc)[NMB][NNB]) {
+  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    const int mb = wm + 2 * mi;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+      if (m < t.rows) {
+        if constexpr (L1) {
+          // gate block c pairs with up block c + NNB/2: the same SwiGLU columns
+#pragma unroll
+          for (int c = 0; c < NNB / 2; ++c) {
+            const float g = acc[mi][c][i], u = acc[mi][c + NNB / 2][i];
+            const float act = g / (1.0f + expf(-g)) * u;
+            const int col = t.n * (NNB * 32) + c * 64 + wn * 32 + lr;
+            const size_t at = (size_t)(t.row0 + m) * P.f + col;
+            if constexpr (FP8) P.Hf[at] = act;  // quantised per 128-column block once it is stored
+            else reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
+          }
+        } else {
+          const int dst = P.row_dst[t.row0 + m];
+#pragma unroll
+          for (int nb = 0; nb < NNB; ++nb) {
+            const int col = t.n * (NNB * 64) + nb * 64 + wn * 32 + lr;
+            P.C[(size_t)dst * P.d + col] = acc[mi][nb][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Drain the last R+1 stages of the ring: stage kt is complete once at most R
+// stages (R * stage_loads loads per lane) are still in flight.
+template <int MB, int NMB, int NNB, bool FP8, int R>
+__device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt, int tid,
+                                      f32x16 (&acc)[NMB > 0 ? NMB : 1][NNB]) {
+  constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8);
+  wait_vmcnt<R * stage_loads(MB, NNB, FP8)>();
+  lds_barrier();
+  if constexpr (NMB > 0) compute_any<MB, NMB, NNB, FP8>(t, lds + rd * SB, kt, tid, acc);
+  if constexpr (R > 0) drain<MB, NMB, NNB, FP8, R - 1>(t, lds, rd + 1 == S ? 0 : rd + 1, kt + 1, tid, acc);
+}
+
+// The whole tile: every wavefront runs the same loads and barriers and owns
+// NMB of the MB row blocks; the accumulators stay inside this function.
+// The LDS ring has ring_stages(MB, NNB) stages of stage_bytes(MB, NNB): as
+// many as fit in 160 KiB (at least 2), so that S-1 stages are in flight per CU.
+// The thread index is made opaque to the optimiser at the start of the tile:
+// the per-lane address offsets derived from it (64-bit row * pitch products)
+// are then computed once per tile instead of being hoisted, for every tile
+// shape of the persistent loop at once, to the kernel entry where they would
+// stay live (and spill) for the whole launch.
+template <int MB, int NMB, int NNB, bool L1, bool FP8>
+__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8), LD = stage_loads(MB, NNB, FP8);
+  static_assert(S >= 2, "the LDS ring needs two stages");
+  f32x16 acc[NMB > 0 ? NMB : 1][NNB];
+#pragma unroll
+  for (int a = 0; a < (NMB > 0 ? NMB : 1); ++a)
+#pragma unroll
+    for (int b = 0; b < NNB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  const int KT = t.ktiles;
+  if (KT < S) {
+    // the whole K extent fits in the ring
+    for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, FP8>(t, kt, lds + kt * SB, tid);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if constexpr (NMB > 0)
+      for (int kt = 0; kt < KT; ++kt) compute_any<MB, NMB, NNB, FP8>(t, lds + kt * SB, kt, tid, acc);
+  } else {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, FP8>(t, s, lds + s * SB, tid);
+    int rd = 0, wr = S - 1, kt = 0;
+    for (; kt + S - 1 < KT; ++kt) {
+      wait_vmcnt<(S - 2) * LD>();  // this lane's loads of stage kt have landed
+      lds_barrier();               // ... everyone's; and slot wr (stage kt-1) is no longer read
+      issue_stage<MB, NNB, FP8>(t, kt + S - 1, lds + wr * SB, tid);
+      if constexpr (NMB > 0) compute_any<MB, NMB, NNB, FP8>(t, lds + rd * SB, kt, tid, acc);
+      rd = rd + 1 == S ? 0 : rd + 1;
+      wr = wr + 1 == S ? 0 : wr + 1;
+    }
+    drain<MB, NMB, NNB, FP8, S - 2>(t, lds, rd, kt, tid, acc);
+  }
+  lds_barrier();  // LDS ring free for the next tile
+  if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc);
+}
+
+// The band's 32-row blocks, rounded up to an even count MB so that both
+// wavefront rows own MB / 2 blocks and one instantiation serves all four
+// wavefronts (rows past the band re-read its last row and are not stored).
+template <int MB, int NNB, bool L1, bool FP8>
+__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+  tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds);
+}
+
+template <int NNB, bool L1, bool FP8>
+__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+  switch ((t.rows + 63) >> 6) {
+    case 1: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
+    case 2: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
+    case 3: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
+    default: run_tile<8, NNB, L1, FP8>(P, t, lds); break;
+  }
+}
+
+// Wait until row band p's H is complete. Thread 0 polls l2_full[p] with
+// device-scope loads (they bypass the CU's L1 and see the value the
+// producers' device-scope atomics left), then the workgroup proceeds.
+//
+// No cache invalidation is needed before the H loads: a band's H lines are
+// first read only after the band is complete (only Linear-2 tiles of band p
+// read them, and only after this wait), rows are whole multiples of 128-byte
+// lines so no line is shared by two bands, and every launch starts with the
+// kernel-entry acquire; so neither this CU's L1 nor its XCD's L2 can hold a
+// stale copy. Invalidating the L2 here would instead discard the weight and
+// activation lines the other 31 CUs of the XCD are reusing.
+__device__ __forceinline__ void wait_row_ready(const GemmParams& P, int p) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&P.l2_full[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < P.ready) {
+      // after one timeout in this call every later wait gives up at once
+      if (__hip_atomic_load(&P.meta[META_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(&P.meta[META_ERR], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Make this workgroup's global stores visible at device scope, then let
+// thread 0 add `inc` to a readiness counter (returned: its old value, in
+// thread 0): every wave waits for its own stores to be
+// acknowledged (vmcnt(0)), the barrier orders that before thread 0, whose
+// device-scope release writes the XCD's L2 back before the increment.
+__device__ __forceinline__ int publish(int32_t* counter, int inc) {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __syncthreads();
+  int old = 0;
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    old = __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return old;
+}
+
+// fp8: quantise column block j (128 SwiGLU columns) of a row band: per row,
+// scale = amax / 448 (1 for an all-zero block) and code = e4m3(value /
+// scale), round to nearest even. 16 lanes per row (8 values each), 16 rows per
+// pass; the loads of four passes are issued before any is used.
+__device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
+  const int rr = threadIdx.x >> 4, q = threadIdx.x & 15;
+  const int col = j * 128 + q * 8;
+  for (int base = 0; base < rows; base += 64) {
+    float4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = base + u * 16 + rr;
+      if (r < rows) {
+        const float4* src = reinterpret_cast<const float4*>(P.Hf + (size_t)(row0 + r) * P.f + col);
+        v[u][0] = src[0];
+        v[u][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = base + u * 16 + rr;
+      if (r >= rows) continue;  // uniform across the 16 lanes of a row
+      const float4 a = v[u][0], b = v[u][1];
+      float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                         fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+      const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a.x / scale, a.y / scale, 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(a.z / scale, a.w / scale, lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b.x / scale, b.y / scale, 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(b.z / scale, b.w / scale, hi, true);
+      *reinterpret_cast<uint2*>(P.H + (size_t)(row0 + r) * P.f + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
+      if (q == 0) P.Hs[(size_t)j * P.cap + row0 + r] = scale;
+    }
+  }
+}
+
+// After a Linear-1 tile's stores. bf16 (fused schedules only): count the tile
+// in l2_full[p]; the band is ready at N1. fp8: the 128-column block j is
+// covered by 128 / (32 nnb1) tiles (2 narrow, 1 wide); each counts itself in
+// blk_done[p][j], and the last of them (every one of the block's Hf stores is
+// then published) quantises the block and counts it in l2_full[p]; the band
+// is ready at f / 128.
+template <bool FP8>
+__device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& t, int p, bool fused, lds_t* lds) {
+  if constexpr (!FP8) {
+    if (fused) publish(P.l2_full + p, 1);
+  } else {
+    const int bn1 = P.nnb1 * 32;
+    const int j = (t.n * bn1) >> 7;
+    const int need = 128 / bn1;
+    __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)lds;
+    const int old = publish(P.blk_done + (size_t)p * (P.f >> 7) + j, 1);
+    if (threadIdx.x == 0) *flag = old;
+    __syncthreads();
+    const bool second = *flag == need - 1;
+    __syncthreads();  // the ring (and the flag in it) is reused by the next tile
+    if (second) {
+      quantize_block(P, t.row0, t.rows, j);
+      publish(P.l2_full + p, 1);
+    }
+  }
+}
+
+template <bool L1, bool FP8>
+__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, bool fused, lds_t* lds) {
+  constexpr int esz = FP8 ? 1 : 2;
+  Tile t;
+  const int e = P.band_expert[p];
+  t.row0 = P.band_row0[p];
+  t.rows = P.band_rows[p];
+  t.n = n;
+  t.cap_stride = P.cap;
+  const int nnb = L1 ? P.nnb1 : P.nnb2;
+  if constexpr (L1) {
+    const int bn = nnb * 32;  // SwiGLU columns: bn gate rows and bn up rows
+    t.lda = (size_t)P.d * esz;
+    t.ldb = (size_t)P.d * esz;
+    t.A = P.X + (size_t)t.row0 * t.lda;
+    const uint8_t* We = P.W1 + (size_t)e * 2 * P.f * t.ldb;
+    t.Bg = We + (size_t)(n * bn) * t.ldb;
+    t.Bu = We + (size_t)(P.f + n * bn) * t.ldb;
+    t.ktiles = P.d * esz / stage_k_bytes(FP8);
+    if constexpr (FP8) {
+      const int db = P.d >> 7, fb2 = (2 * P.f) >> 7;
+      t.As = P.Xs + t.row0;
+      t.Sg = P.W1s + ((size_t)e * fb2 + (n * bn) / 128) * db;
+      t.Su = P.W1s + ((size_t)e * fb2 + (P.f + n * bn) / 128) * db;
+    }
+  } else {
+    const int bn = nnb * 64;  // output columns
+    t.lda = (size_t)P.f * esz;
+    t.ldb = (size_t)P.f * esz;
+    t.A = P.H + (size_t)t.row0 * t.lda;
+    t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * bn) * t.ldb;
+    t.Bu = t.Bg + (size_t)(bn / 2) * t.ldb;
+    t.ktiles = P.f * esz / stage_k_bytes(FP8);
+    if constexpr (FP8) {
+      t.As = P.Hs + t.row0;
+      t.Sg = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn) / 128) * (P.f >> 7);
+      t.Su = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn + bn / 2) / 128) * (P.f >> 7);
+    }
+    if (fused) wait_row_ready(P, p);
+  }
+  if (nnb == 4) dispatch_tile<4, L1, FP8>(P, t, lds);
+  else dispatch_tile<2, L1, FP8>(P, t, lds);
+  if constexpr (L1) finish_l1_tile<FP8>(P, t, p, fused, lds);
+}
+
+// Tile i of a list of nb row bands x N tiles, walked in groups of gm bands:
+// inside a group N-tile by N-tile, the group's bands fastest. Consecutive
+// tiles (which run at the same time, on one XCD) then share gm row bands and
+// a few weight tiles instead of one band and many weight tiles.
+__device__ __forceinline__ void raster(int i, int nb, int N, int gm, int& p, int& n) {
+  const int span = gm * N;
+  const int grp = i / span, base = grp * gm;
+  const int rows = min(gm, nb - base);
+  const int j = i - grp * span;
+  p = base + j % rows;
+  n = j / rows;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(GemmParams P) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+  lds_t* lds = (lds_t*)smem;  // address-space cast to the LDS window
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  // Workgroups are dealt round-robin to the 8 XCDs: make consecutive logical
+  // ids share an XCD so a row band's tiles (same A rows) share one L2.
+  const int lid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int Pb = P.meta[META_P];
+  int p, n;
+  switch (P.mode) {
+    case MODE_SEP_L1:
+      for (int i = lid; i < Pb * P.N1; i += G) {
+        raster(i, Pb, P.N1, P.group_m, p, n);
+        do_tile<true, FP8>(P, p, n, false, lds);
+      }
+      break;
+    case MODE_SEP_L2:
+      for (int i = lid; i < Pb * P.N2; i += G) {
+        raster(i, Pb, P.N2, P.group_m, p, n);
+        do_tile<false, FP8>(P, p, n, false, lds);
+      }
+      break;
+    case MODE_WAVE: {
+      const int nw = P.meta[META_NWAVES];
+      for (int wv = 0; wv < nw; ++wv) {
+        const int pb0 = P.wave_band0[wv], pb1 = P.wave_band0[wv + 1];
+        for (int i = lid; i < (pb1 - pb0) * P.N1; i += G) {
+          raster(i, pb1 - pb0, P.N1, P.group_m, p, n);
+          do_tile<true, FP8>(P, pb0 + p, n, true, lds);
+        }
+        for (int i = lid; i < (pb1 - pb0) * P.N2; i += G) {
+          raster(i, pb1 - pb0, P.N2, P.group_m, p, n);
+          do_tile<false, FP8>(P, pb0 + p, n, true, lds);
+        }
+      }
+      break;
+    }
+    default: {  // MODE_INTERLEAVED
+      const int g = lid >> 1, r = lid & 1, Gp = G >> 1;
+      const int P1 = (P.N1 + 1) >> 1, P2 = (P.N2 + 1) >> 1;
+      const int end1 = Pb * P1, end2 = Pb * P2;
+      int k1 = g, k2 = g;
+      while (k1 < end1 || k2 < end2) {
+        const int p1 = k1 < end1 ? k1 / P1 : 0x3FFFFFFF;
+        const int p2 = k2 / P2;
+        if (k2 < end2 && p2 + P.lead_D <= p1) {
+          const int n = 2 * (k2 % P2) + r;
+          if (n < P.N2) do_tile<false, FP8>(P, p2, n, true, lds);
+          k2 += Gp;
+        } else {
+          const int n = 2 * (k1 % P1) + r;
+          if (n < P.N1) do_tile<true, FP8>(P, p1, n, true, lds);
+          k1 += Gp;
+        }
+      }
+      break;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe

@@ -10,13 +10,10 @@
 
 namespace moe {
 
-// Grouped-GEMM tiling (bf16 and fp8 share the byte layout of a stage: 128
-// bytes of K per row, i.e. 64 bf16 or 128 e4m3 values).
+// Grouped-GEMM tiling. A tile holds NNB * 64 weight rows, NNB = 2 (narrow) or
+// 4 (wide): a Linear-1 tile covers NNB * 32 SwiGLU columns (as many gate rows
+// plus as many up rows), a Linear-2 tile NNB * 64 output columns.
 constexpr int kBM = 256;          // rows per row band (scheduler row)
-constexpr int kBN1 = 64;          // SwiGLU output columns per Linear-1 tile (64 gate + 64 up W1 rows)
-constexpr int kBN2 = 128;         // output columns per Linear-2 tile
-constexpr int kBNW = 128;         // weight rows per tile
-constexpr int kKBytes = 128;      // K bytes per row per pipeline stage
 constexpr int kGemmThreads = 256; // 4 wavefronts
 constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
@@ -117,6 +114,13 @@ hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, cons
 
 // Persistent-grid size for the grouped GEMM on the current device.
 int gemm_grid(const moe_problem_t& p);
+
+// Expert-GEMM tile widths (nnb1, nnb2: 2 = 128 weight rows per tile, 4 = 256)
+// and row bands per raster group, from the problem's flags and shape.
+struct TileChoice {
+  int nnb1, nnb2, group_m;
+};
+TileChoice choose_tiles(const moe_problem_t& p, const Layout& L, int G);
 
 // Shared device helpers -------------------------------------------------------
 

@@ -84,8 +84,17 @@ typedef enum {
                                      leads by at least lead_D rows, otherwise a Linear-1 tile */
 } moe_sched_t;
 
+/* Tile-shape controls of the grouped expert GEMMs. Every combination gives
+ * bit-identical results (each output element is computed by one tile with the
+ * same K order); they exist for tests and tuning. By default the widths and
+ * the raster order are chosen from the shape. */
 enum {
-  MOE_FLAG_NONE = 0u
+  MOE_FLAG_NONE = 0u,
+  MOE_FLAG_TILE_NARROW = 1u,      /* every tile 128 weight rows wide */
+  MOE_FLAG_TILE_WIDE = 2u,        /* 256 weight rows wide wherever the shape allows (Linear-2 tiles need
+                                     d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
+  MOE_FLAG_BAND_MAJOR = 4u        /* walk the separate and expert-wave tile lists row band by row band
+                                     instead of in groups of bands */
 };
 
 typedef struct moe_problem {
@@ -105,7 +114,7 @@ typedef struct moe_problem {
   int32_t wave_experts;  /* expert-wave: experts per wave; 0 = fewest experts whose Linear-1
                             tiles fill the persistent grid */
   int32_t grid;          /* persistent workgroups; 0 = one per compute unit */
-  uint32_t flags;        /* MOE_FLAG_* (none defined yet; must be 0) */
+  uint32_t flags;        /* MOE_FLAG_* bits; 0 = tile shapes chosen from the problem's shape */
 } moe_problem_t;
 
 /* Byte offsets of the intermediates inside a workspace (for inspection by

@@ -52,11 +52,14 @@ def test_fp8_dispatch_codes_and_scales_exact(name):
     np.testing.assert_array_equal(v["x_perm_scale"].numpy()[:, :A], xs[tok // 128].T)
 
 
+@pytest.mark.parametrize("tiles", ["narrow", "wide"])
 @pytest.mark.parametrize("name", list(FP8))
-def test_fp8_h_quantiser_bit_exact(name):
+def test_fp8_h_quantiser_bit_exact(name, tiles):
+    """Narrow Linear-1 tiles cover half a 128-column block each (the second one
+    quantises it), wide tiles a whole block."""
     import expert_grouped_gemm_amd as moe
     cfg = FP8[name]
-    inp, g, p, Y, Y32, ws = _run(cfg)
+    inp, g, p, Y, Y32, ws = _run(cfg, tiles=tiles)
     v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items()}
     A = int(v["meta"][0])
     hf = v["h_f32"].numpy()[:A].astype(np.float32)
@@ -69,11 +72,12 @@ def test_fp8_h_quantiser_bit_exact(name):
     np.testing.assert_array_equal(v["h"].numpy()[:A], codes)
 
 
+@pytest.mark.parametrize("tiles", ["narrow", "wide"])
 @pytest.mark.parametrize("sched", ["separate", "expert_wave", "interleaved"])
 @pytest.mark.parametrize("name", list(FP8))
-def test_fp8_layer_y_parity(name, sched):
+def test_fp8_layer_y_parity(name, sched, tiles):
     cfg = FP8[name]
-    inp, g, p, Y, Y32, ws = _run(cfg, sched=sched)
+    inp, g, p, Y, Y32, ws = _run(cfg, sched=sched, tiles=tiles)
     ref = oracle.moe_layer(inp, cfg)
     stats = check_y(Y.float().cpu().numpy(), ref["Y"], fp8=True, label=f"{name}/{sched}")
     # the same quantisation on both sides: far inside the 3e-2 budget
@@ -84,7 +88,9 @@ def test_fp8_schedule_invariance_bitwise():
     cfg = FP8["fp8_multi_band"]
     g = to_gpu(moe_synth.generate(cfg))
     base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
-    for kw in (dict(sched="expert_wave"), dict(sched="interleaved"), dict(sched="interleaved", lead_D=1, grid=8)):
+    for kw in (dict(sched="expert_wave"), dict(sched="interleaved"), dict(sched="interleaved", lead_D=1, grid=8),
+               dict(sched="separate", tiles="wide"), dict(sched="interleaved", tiles="wide"),
+               dict(sched="separate", tiles="narrow", band_major=True)):
         Y, _, _ = run_layer(problem_of(cfg, **kw), g, want_fp32=False)
         assert torch.equal(Y.view(torch.int16), base.view(torch.int16)), kw
 
@@ -96,7 +102,8 @@ def test_fp8_fused_schedules_never_read_stale_h():
     cfg = FP8["fp8_small_segments"]
     g = to_gpu(moe_synth.generate(cfg))
     base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
-    for kw in (dict(sched="interleaved"), dict(sched="interleaved", lead_D=1), dict(sched="expert_wave")):
+    for kw in (dict(sched="interleaved"), dict(sched="interleaved", lead_D=1), dict(sched="expert_wave"),
+               dict(sched="interleaved", tiles="wide"), dict(sched="expert_wave", tiles="wide")):
         p = problem_of(cfg, **kw)
         ws = moe.alloc_workspace(p)
         for _ in range(3):

@@ -70,6 +70,16 @@ def test_layer_y_parity(name, sched):
     check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=f"{name}/{sched}")
 
 
+@pytest.mark.parametrize("tiles", ["narrow", "wide"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_share", "multi_band", "zipf_small"])
+def test_layer_y_parity_tile_widths(name, tiles):
+    """Both expert-GEMM tile widths against the oracle (wide Linear-2 tiles
+    need d % 256 == 0: ragged_share, d = 384, keeps narrow Linear-2 tiles)."""
+    cfg = SMALL[name]
+    inp, ref, p, Y, Y32, ws = _oracle_and_gpu(cfg, sched="separate", tiles=tiles)
+    check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=f"{name}/{tiles}")
+
+
 def test_router_standalone_with_ties_and_counts():
     """moe_route_topk on its own, with constructed ties at the k-th boundary and
     -0.0 / +0.0 pairs; global counts sum to T*k."""
@@ -136,7 +146,12 @@ def test_schedule_and_grid_invariance_bitwise(name):
     variants = [dict(sched="expert_wave"), dict(sched="expert_wave", wave_experts=1),
                 dict(sched="interleaved", lead_D=1), dict(sched="interleaved", lead_D=3),
                 dict(sched="interleaved"), dict(sched="interleaved", grid=6), dict(sched="expert_wave", grid=10),
-                dict(sched="separate", grid=2)]
+                dict(sched="separate", grid=2),
+                # tile widths and raster orders: the same tiles' K order, so the same bits
+                dict(sched="separate", tiles="wide"), dict(sched="separate", tiles="narrow", band_major=True),
+                dict(sched="separate", tiles="wide", band_major=True, grid=10),
+                dict(sched="expert_wave", tiles="wide"), dict(sched="interleaved", tiles="wide"),
+                dict(sched="interleaved", tiles="wide", lead_D=1, grid=8), dict(sched="interleaved", tiles="narrow")]
     for kw in variants:
         p = problem_of(cfg, **kw)
         Y, _, ws2 = run_layer(p, g, want_fp32=False)
@@ -180,7 +195,8 @@ def test_fused_schedules_never_read_stale_h(name):
     g = to_gpu(moe_synth.generate(cfg))
     base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
     for kw in (dict(sched="interleaved"), dict(sched="interleaved", lead_D=1), dict(sched="expert_wave"),
-               dict(sched="interleaved", grid=16)):
+               dict(sched="interleaved", grid=16), dict(sched="interleaved", tiles="wide"),
+               dict(sched="expert_wave", tiles="wide")):
         p = problem_of(cfg, **kw)
         ws = moe.alloc_workspace(p)
         for _ in range(3):

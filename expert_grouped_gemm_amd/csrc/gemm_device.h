@@ -399,10 +399,16 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
     for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, FP8>(t, s, lds + s * SB, tid);
     int rd = 0, wr = S - 1, kt = 0;
     for (; kt + S - 1 < KT; ++kt) {
-      wait_vmcnt<(S - 2) * LD>();  // this lane's loads of stage kt have landed
-      lds_barrier();               // ... everyone's; and slot wr (stage kt-1) is no longer read
+      // Slot wr held stage kt-1, which every wavefront finished reading
+      // before the barrier that closed the previous step: refill it first,
+      // so S-1 stages stay in flight while this one is awaited (the memory
+      // system bounds the requests a CU may have outstanding; letting the
+      // queue drain at every step would waste that bound).
       issue_stage<MB, NNB, FP8>(t, kt + S - 1, lds + wr * SB, tid);
+      wait_vmcnt<(S - 1) * LD>();  // this lane's loads of stage kt have landed
+      lds_barrier();               // ... everyone's
       if constexpr (NMB > 0) compute_any<MB, NMB, NNB, FP8>(t, lds + rd * SB, kt, tid, acc);
+      lds_barrier();               // slot rd is free for the refill of the next step
       rd = rd + 1 == S ? 0 : rd + 1;
       wr = wr + 1 == S ? 0 : wr + 1;
     }

@@ -75,7 +75,7 @@ def gemm_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg, sched):
+def measured_traffic(cfg, sched, tiles="auto", band_major=False):
     """HBM bytes per grouped-GEMM launch measured with rocprofv3 FETCH_SIZE /
     WRITE_SIZE (scaled by a plain-copy calibration) for this workload and
     schedule, as recorded in profiles/gemm_traffic_<workload>_<sched>.md; null
@@ -89,7 +89,7 @@ def measured_traffic(cfg, sched):
         blob = json.loads(text.split("```json")[1].split("```")[0])
     except (IndexError, ValueError):
         return None
-    if blob.get("gemm_source_sha256_16") != digest:
+    if blob.get("gemm_source_sha256_16") != digest or blob.get("tiles", "auto") != tiles or band_major:
         return None
     return blob.get("hbm_bytes_per_launch")
 
@@ -210,7 +210,7 @@ def main():
             "peak": rpeak,
             "unit": runit,
             "frac": round(achieved / rpeak, 4),
-            "traffic": measured_traffic(cfg, args.sched),
+            "traffic": measured_traffic(cfg, args.sched, args.tiles, args.band_major),
             "algorithmic_bytes_per_launch": gb,
             "useful_flop_per_launch": useful_flop,
             "arithmetic_intensity_flop_per_byte": round(intensity, 1),

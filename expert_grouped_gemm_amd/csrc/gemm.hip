@@ -86,7 +86,7 @@ int gemm_grid(const moe_problem_t& p) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel_bf16(),
-                                                     kGemmThreads, 0) != hipSuccess)
+                                                     gemm_threads(false), 0) != hipSuccess)
       return 0;
     cached_grid = prop.multiProcessorCount * (occ > 0 ? occ : 1);
     cached_dev = dev;

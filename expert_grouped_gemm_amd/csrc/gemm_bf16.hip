@@ -4,7 +4,7 @@
 namespace moe {
 
 hipError_t launch_gemm_bf16(const GemmParams& P, int G, hipStream_t s) {
-  hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(G), dim3(kGemmThreads), 0, s, P);
+  hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(G), dim3(gemm_threads(false)), 0, s, P);
   return hipGetLastError();
 }
 

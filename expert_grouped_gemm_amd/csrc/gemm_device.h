@@ -21,11 +21,15 @@
 //     as many stages as fit in 160 KiB, filled by direct global->LDS loads
 //     (global_load_lds_dwordx4), so the weight tile is read once per band and
 //     reused by every row of the band;
-//   - 4 wavefronts, 2 (rows) x 2 (columns); a wavefront owns the 32-row
-//     blocks {wm, wm+2, ...} of the band and NNB 32-column blocks, one
-//     v_mfma_f32_32x32x16_bf16 accumulator each; the number of 32-row blocks
-//     (rounded up to even) is a template parameter, so a short band costs
-//     fewer loads and MFMAs;
+//   - 8 wavefronts, two per SIMD (while one waits on LDS or on its loads the
+//     other issues MFMAs), in a WM (rows) x WN (columns) grid: 2 x 4 for
+//     wide tiles, 4 x 2 for narrow ones. A wavefront owns the 32-row blocks
+//     {wm, wm+WM, ...} of the band and, in each half of the weight rows,
+//     NNB/WN 32-column blocks, one v_mfma_f32_32x32x16_bf16 accumulator each;
+//     a Linear-1 wavefront thus holds the gate and the up column of every
+//     SwiGLU output it owns. The number of 32-row blocks (rounded up to a
+//     multiple of WM) is a template parameter, so a short band costs fewer
+//     loads and MFMAs;
 //   - in the separate and expert-wave schedules the tile list is walked in
 //     groups of group_m row bands, N-tile by N-tile inside a group, so the
 //     tiles that run at the same time on one XCD share both their row bands
@@ -142,7 +146,29 @@ __host__ __device__ constexpr int ring_stages(int MB, int NNB, bool FP8) {
 // global -> LDS loads issued per lane per stage (16 bytes each, plus one
 // 4-byte row-scale load with fp8)
 __host__ __device__ constexpr int stage_loads(int MB, int NNB, bool FP8) {
-  return (MB * 32 + NNB * 64) * stage_k_bytes(FP8) / (kGemmThreads * 16) + (FP8 ? 1 : 0);
+  return (MB * 32 + NNB * 64) * stage_k_bytes(FP8) / (gemm_threads(FP8) * 16) + (FP8 ? 1 : 0);
+}
+
+// Wavefront grid of a tile of width NNB: WM wavefront rows x WN wavefront
+// columns; each wavefront owns CPH = NNB / WN 32-column blocks in each half
+// of the tile's weight rows (half = NNB * 32 rows: the gate rows of a
+// Linear-1 tile, or the first half of a Linear-2 tile's output columns).
+template <int NNB, bool FP8>
+struct WaveGrid {
+  static constexpr int W = gemm_threads(FP8) / 64;
+  static_assert(W == 4 || W == 8, "wavefront grid");
+  static constexpr int WN = (W == 8 && NNB == 4) ? 4 : 2;
+  static constexpr int WM = W / WN;
+  static constexpr int CPH = NNB / WN;
+  static constexpr int NCB = 2 * CPH;  // accumulator columns per wavefront
+  static_assert(CPH >= 1, "a wavefront owns at least one block per half");
+};
+
+// Weight row (tile-relative) of column block c of half h owned by wavefront
+// column wn, for lane row lr; the same index gives the output column.
+template <int NNB, bool FP8>
+__device__ __forceinline__ int wave_col(int h, int c, int wn, int lr) {
+  return h * (NNB * 32) + (c * WaveGrid<NNB, FP8>::WN + wn) * 32 + lr;
 }
 
 // 16-byte chunk c of row `row` in a stage of KB-byte rows. The chunk index is
@@ -183,27 +209,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int MB, int NNB, bool FP8>
 __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
   constexpr int KB = stage_k_bytes(FP8), CH = KB / 16, RPI = 64 / CH;
-  constexpr int NA = MB * 32 / (4 * RPI), NBW = NNB * 64 / (4 * RPI), half = NNB * 32;
+  constexpr int NW = gemm_threads(FP8) / 64;
+  constexpr int NA = MB * 32 / (NW * RPI), NBW = NNB * 64 / (NW * RPI), half = NNB * 32;
+  static_assert(NA * NW * RPI == MB * 32 && NBW * NW * RPI == NNB * 64, "stage rows per wavefront");
   const int w = tid >> 6, lane = tid & 63;
   const int kb = kt * KB;
   const int sub = lane / CH, slot = lane % CH;
   if (j < NA) {
-    const int r0 = (j * 4 + w) * RPI;
+    const int r0 = (j * NW + w) * RPI;
     const int r = r0 + sub;
     const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
     const uint8_t* g = t.A + (size_t)gr * t.lda + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
     __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
   } else if (j < NA + NBW) {
-    const int r0 = ((j - NA) * 4 + w) * RPI;
+    const int r0 = ((j - NA) * NW + w) * RPI;
     const int r = r0 + sub;
     const uint8_t* base = r < half ? t.Bg : t.Bu;
     const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
     __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + r0 * KB, 16, 0, 0);
   } else if constexpr (FP8) {
-    const int r = w * 64 + lane;
+    // the 256 row scales: kBM / NW per wavefront, one 4-byte lane each
+    constexpr int PER = kBM / NW;
+    const int r = w * PER + lane;
     const int gr = r < t.rows ? r : t.rows - 1;
     const float* g = t.As + (size_t)kt * t.cap_stride + gr;
-    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + w * 256, 4, 0, 0);
+    if (lane < PER)
+      __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + w * PER * 4, 4, 0, 0);
   }
 }
 
@@ -219,23 +250,25 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, in
 // half h of an MFMA reads the same chunk indices of its A row and B row), so
 // the sum over K is unchanged.
 template <int NMB, int NNB>
-__device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, int tid, f32x16 (&acc)[NMB][NNB]) {
+__device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, int tid,
+                                              f32x16 (&acc)[NMB][WaveGrid<NNB, false>::NCB]) {
+  using G = WaveGrid<NNB, false>;
   constexpr int KB = stage_k_bytes(false);
-  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < KB / 32; ++ks) {
     const int chunk = ks * 2 + hi;
-    bf16x8 b[NNB];
+    bf16x8 b[G::NCB];
 #pragma unroll
-    for (int nb = 0; nb < NNB; ++nb)
-      b[nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(nb * 64 + wn * 32 + lr, chunk));
+    for (int nb = 0; nb < G::NCB; ++nb)
+      b[nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(wave_col<NNB, false>(nb / G::CPH, nb % G::CPH, wn, lr), chunk));
 #pragma unroll
     for (int mi = 0; mi < NMB; ++mi) {
-      const int row = (wm + 2 * mi) * 32 + lr;
+      const int row = (wm + G::WM * mi) * 32 + lr;
       const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off<KB>(row, chunk));
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
+      for (int nb = 0; nb < G::NCB; ++nb)
         acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mi][nb], 0, 0, 0);
     }
   }
@@ -254,24 +287,26 @@ __device__ __forceinline__ i32x8 lds_read_32B(const lds_t* base, int row, int ch
 // the first half of the weight rows and swu for the second.
 template <int NMB, int NNB>
 __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* sb, const lds_t* ss, float swg,
-                                                  float swu, int tid, f32x16 (&acc)[NMB][NNB]) {
-  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+                                                  float swu, int tid, f32x16 (&acc)[NMB][WaveGrid<NNB, true>::NCB]) {
+  using G = WaveGrid<NNB, true>;
+  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
-  i32x8 b[2][NNB];
+  i32x8 b[2][G::NCB];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int nb = 0; nb < NNB; ++nb) b[ks][nb] = lds_read_32B(sb, nb * 64 + wn * 32 + lr, ks * 4 + hi * 2);
+    for (int nb = 0; nb < G::NCB; ++nb)
+      b[ks][nb] = lds_read_32B(sb, wave_col<NNB, true>(nb / G::CPH, nb % G::CPH, wn, lr), ks * 4 + hi * 2);
   const f32x16 zero = {};
 #pragma unroll
   for (int mi = 0; mi < NMB; ++mi) {
-    const int mb = wm + 2 * mi;
-    f32x16 part[NNB];
+    const int mb = wm + G::WM * mi;
+    f32x16 part[G::NCB];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const i32x8 a = lds_read_32B(sa, mb * 32 + lr, ks * 4 + hi * 2);
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
+      for (int nb = 0; nb < G::NCB; ++nb)
         part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[ks][nb], ks ? part[nb] : zero, 0, 0, 0,
                                                                    127, 0, 127);
     }
@@ -283,8 +318,8 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g + j;
 #pragma unroll
-        for (int nb = 0; nb < NNB; ++nb)
-          acc[mi][nb][i] = fmaf(part[nb][i], sx[j] * (nb < NNB / 2 ? swg : swu), acc[mi][nb][i]);
+        for (int nb = 0; nb < G::NCB; ++nb)
+          acc[mi][nb][i] = fmaf(part[nb][i], sx[j] * (nb < G::CPH ? swg : swu), acc[mi][nb][i]);
       }
     }
   }
@@ -302,7 +337,7 @@ __device__ __forceinline__ float uniform_load(const float* p, int i) {
 
 template <int MB, int NMB, int NNB, bool FP8>
 __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int tid,
-                                            f32x16 (&acc)[NMB][NNB]) {
+                                            f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
   if constexpr (FP8) {
     const float swg = uniform_load(t.Sg, kt), swu = uniform_load(t.Su, kt);
     static_assert(stage_k_bytes(true) == 128, "an fp8 stage is one 128-wide scale block");
@@ -317,23 +352,24 @@ __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int 
 // column lane%32.
 template <int NMB, int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
-                                         const f32x16 (&acc)[NMB][NNB]) {
-  const int lane = tid & 63, wm = (tid >> 6) & 1, wn = tid >> 7;
+                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
+  using G = WaveGrid<NNB, FP8>;
+  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int mi = 0; mi < NMB; ++mi) {
-    const int mb = wm + 2 * mi;
+    const int mb = wm + G::WM * mi;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
       if (m < t.rows) {
         if constexpr (L1) {
-          // gate block c pairs with up block c + NNB/2: the same SwiGLU columns
+          // gate block c pairs with up block c of the second half: the same SwiGLU columns
 #pragma unroll
-          for (int c = 0; c < NNB / 2; ++c) {
-            const float g = acc[mi][c][i], u = acc[mi][c + NNB / 2][i];
+          for (int c = 0; c < G::CPH; ++c) {
+            const float g = acc[mi][c][i], u = acc[mi][G::CPH + c][i];
             const float act = g / (1.0f + expf(-g)) * u;
-            const int col = t.n * (NNB * 32) + c * 64 + wn * 32 + lr;
+            const int col = t.n * (NNB * 32) + wave_col<NNB, FP8>(0, c, wn, lr);
             const size_t at = (size_t)(t.row0 + m) * P.f + col;
             if constexpr (FP8) P.Hf[at] = act;  // quantised per 128-column block once it is stored
             else reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
@@ -341,8 +377,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
         } else {
           const int dst = P.row_dst[t.row0 + m];
 #pragma unroll
-          for (int nb = 0; nb < NNB; ++nb) {
-            const int col = t.n * (NNB * 64) + nb * 64 + wn * 32 + lr;
+          for (int nb = 0; nb < G::NCB; ++nb) {
+            const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
             P.C[(size_t)dst * P.d + col] = acc[mi][nb][i];
           }
         }
@@ -355,7 +391,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
 // stages (R * stage_loads loads per lane) are still in flight.
 template <int MB, int NMB, int NNB, bool FP8, int R>
 __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt, int tid,
-                                      f32x16 (&acc)[NMB > 0 ? NMB : 1][NNB]) {
+                                      f32x16 (&acc)[NMB > 0 ? NMB : 1][WaveGrid<NNB, FP8>::NCB]) {
   constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8);
   wait_vmcnt<R * stage_loads(MB, NNB, FP8)>();
   lds_barrier();
@@ -378,11 +414,11 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
   asm volatile("" : "+v"(tid));
   constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8), LD = stage_loads(MB, NNB, FP8);
   static_assert(S >= 2, "the LDS ring needs two stages");
-  f32x16 acc[NMB > 0 ? NMB : 1][NNB];
+  f32x16 acc[NMB > 0 ? NMB : 1][WaveGrid<NNB, FP8>::NCB];
 #pragma unroll
   for (int a = 0; a < (NMB > 0 ? NMB : 1); ++a)
 #pragma unroll
-    for (int b = 0; b < NNB; ++b)
+    for (int b = 0; b < WaveGrid<NNB, FP8>::NCB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
@@ -418,21 +454,29 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
   if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc);
 }
 
-// The band's 32-row blocks, rounded up to an even count MB so that both
-// wavefront rows own MB / 2 blocks and one instantiation serves all four
-// wavefronts (rows past the band re-read its last row and are not stored).
+// The band's 32-row blocks, rounded up to a multiple MB of the wavefront
+// rows WM so that every wavefront row owns MB / WM blocks and one
+// instantiation serves all wavefronts (rows past the band re-read its last
+// row and are not stored).
 template <int MB, int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
-  tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds);
+  static_assert(MB % WaveGrid<NNB, FP8>::WM == 0, "row blocks per wavefront row");
+  tile_body<MB, MB / WaveGrid<NNB, FP8>::WM, NNB, L1, FP8>(P, t, lds);
 }
 
 template <int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
-  switch ((t.rows + 63) >> 6) {
-    case 1: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
-    case 2: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
-    case 3: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
-    default: run_tile<8, NNB, L1, FP8>(P, t, lds); break;
+  if constexpr (WaveGrid<NNB, FP8>::WM == 2) {
+    switch ((t.rows + 63) >> 6) {
+      case 1: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
+      case 2: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
+      case 3: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
+      default: run_tile<8, NNB, L1, FP8>(P, t, lds); break;
+    }
+  } else {
+    static_assert(WaveGrid<NNB, FP8>::WM == 4, "wavefront rows");
+    if (t.rows <= 128) run_tile<4, NNB, L1, FP8>(P, t, lds);
+    else run_tile<8, NNB, L1, FP8>(P, t, lds);
   }
 }
 
@@ -481,16 +525,18 @@ __device__ __forceinline__ int publish(int32_t* counter, int inc) {
 
 // fp8: quantise column block j (128 SwiGLU columns) of a row band: per row,
 // scale = amax / 448 (1 for an all-zero block) and code = e4m3(value /
-// scale), round to nearest even. 16 lanes per row (8 values each), 16 rows per
-// pass; the loads of four passes are issued before any is used.
+// scale), round to nearest even. 16 lanes per row (8 values each), one row
+// per 16 threads per pass; the loads of four passes are issued before any is
+// used.
 __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
+  constexpr int RPP = gemm_threads(true) / 16;  // rows per pass
   const int rr = threadIdx.x >> 4, q = threadIdx.x & 15;
   const int col = j * 128 + q * 8;
-  for (int base = 0; base < rows; base += 64) {
+  for (int base = 0; base < rows; base += 4 * RPP) {
     float4 v[4][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = base + u * 16 + rr;
+      const int r = base + u * RPP + rr;
       if (r < rows) {
         const float4* src = reinterpret_cast<const float4*>(P.Hf + (size_t)(row0 + r) * P.f + col);
         v[u][0] = src[0];
@@ -499,7 +545,7 @@ __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = base + u * 16 + rr;
+      const int r = base + u * RPP + rr;
       if (r >= rows) continue;  // uniform across the 16 lanes of a row
       const float4 a = v[u][0], b = v[u][1];
       float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
@@ -603,7 +649,7 @@ __device__ __forceinline__ void raster(int i, int nb, int N, int gm, int& p, int
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(GemmParams P) {
+__global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   lds_t* lds = (lds_t*)smem;  // address-space cast to the LDS window
   const int G = gridDim.x;

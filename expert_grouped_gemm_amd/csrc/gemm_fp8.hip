@@ -4,7 +4,7 @@
 namespace moe {
 
 hipError_t launch_gemm_fp8(const GemmParams& P, int G, hipStream_t s) {
-  hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(G), dim3(kGemmThreads), 0, s, P);
+  hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(G), dim3(gemm_threads(true)), 0, s, P);
   return hipGetLastError();
 }
 

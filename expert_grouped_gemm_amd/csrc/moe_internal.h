@@ -14,7 +14,10 @@ namespace moe {
 // 4 (wide): a Linear-1 tile covers NNB * 32 SwiGLU columns (as many gate rows
 // plus as many up rows), a Linear-2 tile NNB * 64 output columns.
 constexpr int kBM = 256;          // rows per row band (scheduler row)
-constexpr int kGemmThreads = 256; // 4 wavefronts
+// Threads of the expert-GEMM workgroup: bf16 runs 8 wavefronts (two per
+// SIMD, 256 registers each); fp8 needs more registers per wavefront (block
+// partial sums next to the accumulators) and runs 4 (one per SIMD).
+constexpr int gemm_threads(bool fp8) { return fp8 ? 256 : 512; }
 constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
 constexpr int kMetaInts = 64;

@@ -119,6 +119,7 @@ struct Tile {
   int row0;               // first X_perm / H row of the band
   int n;                  // N-tile index
   int ktiles;             // K bytes / stage_k_bytes
+  int krot;               // pipeline stage kt streams K slice (kt + krot) mod ktiles
   // fp8 only
   const float* As;        // row scales of K block 0 for the band's first row (next block: + cap)
   const float* Sg;        // weight block scales of the first half along K (one per 128-byte stage)
@@ -238,10 +239,29 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
   }
 }
 
+// The K loop of every Linear-2 tile of local expert e starts at slice
+// (e * kKRot) mod ktiles and wraps around. The tiles running at the same time
+// on different XCDs (different experts' bands) then stream different column
+// offsets of their weight rows; at a power-of-two row pitch (W2 rows of 2 f
+// bytes) they would otherwise all hit the same HBM channels together.
+// Measured: the Linear-2 launch of the DeepSeek-style share (4 KiB rows)
+// 10-13% faster; Linear-1, whose rows are d elements long, gained nothing and
+// does not rotate. The start depends on the expert alone, not on the band a
+// row falls in, so every output element is summed in one fixed K order
+// whatever the tile width, schedule, grid or the order of the tokens.
+constexpr int kKRot = 5;
+
+// K slice streamed by pipeline stage kt of tile t.
+__device__ __forceinline__ int kslice(const Tile& t, int kt) {
+  const int s = kt + t.krot;
+  return s >= t.ktiles ? s - t.ktiles : s;
+}
+
 template <int MB, int NNB, bool FP8>
 __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, int tid) {
+  const int ks = kslice(t, kt);
 #pragma unroll
-  for (int j = 0; j < stage_loads(MB, NNB, FP8); ++j) issue_load<MB, NNB, FP8>(t, kt, st, tid, j);
+  for (int j = 0; j < stage_loads(MB, NNB, FP8); ++j) issue_load<MB, NNB, FP8>(t, ks, st, tid, j);
 }
 
 // MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
@@ -339,7 +359,8 @@ template <int MB, int NMB, int NNB, bool FP8>
 __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int tid,
                                             f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
   if constexpr (FP8) {
-    const float swg = uniform_load(t.Sg, kt), swu = uniform_load(t.Su, kt);
+    const int ks = kslice(t, kt);
+    const float swg = uniform_load(t.Sg, ks), swu = uniform_load(t.Su, ks);
     static_assert(stage_k_bytes(true) == 128, "an fp8 stage is one 128-wide scale block");
     compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8),
                                 swg, swu, tid, acc);
@@ -609,6 +630,7 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, bool 
     t.Bg = We + (size_t)(n * bn) * t.ldb;
     t.Bu = We + (size_t)(P.f + n * bn) * t.ldb;
     t.ktiles = P.d * esz / stage_k_bytes(FP8);
+    t.krot = 0;
     if constexpr (FP8) {
       const int db = P.d >> 7, fb2 = (2 * P.f) >> 7;
       t.As = P.Xs + t.row0;
@@ -623,6 +645,7 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, bool 
     t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * bn) * t.ldb;
     t.Bu = t.Bg + (size_t)(bn / 2) * t.ldb;
     t.ktiles = P.f * esz / stage_k_bytes(FP8);
+    t.krot = (e * kKRot) % t.ktiles;
     if constexpr (FP8) {
       t.As = P.Hs + t.row0;
       t.Sg = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn) / 128) * (P.f >> 7);

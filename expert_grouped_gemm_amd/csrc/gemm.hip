@@ -44,17 +44,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   const int first = sh[wv] + x - nb;
+  __shared__ int row_off[1025];
   if (e < El) {
     start[e] = first;
-    const int r0 = offsets[e];
-    for (int i = 0; i < nb; ++i) {
-      band_expert[first + i] = e;
-      band_row0[first + i] = r0 + i * kBM;
-      band_rows[first + i] = min(kBM, cnt - i * kBM);
-    }
+    row_off[e] = offsets[e];
   }
-  if (threadIdx.x == 0) start[El] = sh[16];
+  if (threadIdx.x == 0) {
+    start[El] = sh[16];
+    row_off[El] = offsets[El];
+  }
   __syncthreads();
+  // band table, one band per thread: band q belongs to the last expert whose
+  // first band is <= q (binary search over start[]; experts without rows have
+  // start[e] == start[e + 1] and are skipped)
+  for (int q = threadIdx.x; q < start[El]; q += blockDim.x) {
+    int lo = 0, hi = El - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= q) lo = mid;
+      else hi = mid - 1;
+    }
+    const int i = q - start[lo];
+    band_expert[q] = lo;
+    band_row0[q] = row_off[lo] + i * kBM;
+    band_rows[q] = min(kBM, row_off[lo + 1] - row_off[lo] - i * kBM);
+  }
   if (threadIdx.x == 0) {
     const int Ptot = start[El];
     meta[META_P] = Ptot;

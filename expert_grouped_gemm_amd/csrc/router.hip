@@ -5,10 +5,15 @@
 // logits.
 //
 // One wavefront per token. Each lane holds ceil(E/64) logits (E <= 1024, so
-// at most 16). Selection runs k rounds of a wave-wide max over 64-bit keys
-// (order-preserving fp32 bits << 32 | ~expert), so the larger logit wins and
-// equal logits go to the lower expert index; -0.0 is folded into +0.0 first
-// so that the two tie. Memory traffic is one coalesced read of the logits row.
+// at most 16); lane l's slot i is expert l + 64 i. Selection runs k rounds:
+// each lane proposes its largest untaken logit (the lowest slot among equal
+// ones), a wave-wide fp32 max finds the round's value, and a wave-wide min
+// over the expert index of the lanes that hold it breaks ties toward the
+// lower expert. -0.0 compares equal to +0.0, so the two tie. Both wave
+// reductions use in-row DPP moves and four lane reads, no LDS round trips.
+// Memory traffic is one coalesced read of the logits row.
+#include <limits.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -16,26 +21,33 @@ namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7FFFFFFFu) == 0) u = 0;                       // -0.0 ties +0.0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);          // monotone in v
-  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
 
-// Inverse of the order-preserving map: the logit a key was built from.
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t o = (uint32_t)(key >> 32);
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+// Every lane's value combined over its 16-lane row (quad swaps, then the
+// half-row and row mirrors), then the four rows through lane reads.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, __int_as_float(dpp<0xB1>(__float_as_int(x))));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, __int_as_float(dpp<0x4E>(__float_as_int(x))));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, __int_as_float(dpp<0x141>(__float_as_int(x))));  // row_half_mirror
+  x = fmaxf(x, __int_as_float(dpp<0x140>(__float_as_int(x))));  // row_mirror
+  const int xi = __float_as_int(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t y = __shfl_xor(x, off, 64);
-    x = y > x ? y : x;
-  }
-  return x;
+__device__ __forceinline__ int wave_min_i32(int x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  x = min(x, dpp<0x140>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
@@ -44,48 +56,46 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                                                          int32_t* __restrict__ counts_global) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= T) return;  // whole wavefronts: the DPP reductions need every lane
   const float* row = logits + (size_t)t * E;
 
   constexpr int kMaxPer = 16;
   float v[kMaxPer];
   const int per = (E + 63) >> 6;
+  uint32_t taken = 0;  // bit i: slot i of this lane already selected (or absent)
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? row[e] : 0.0f;
+    const bool present = i < per && e < E;
+    v[i] = present ? row[e] : 0.0f;
+    if (!present) taken |= 1u << i;
   }
-  uint32_t taken = 0;  // bit i: slot i of this lane already selected (or absent)
-#pragma unroll
-  for (int i = 0; i < kMaxPer; ++i)
-    if (!(i < per && lane + 64 * i < E)) taken |= 1u << i;
 
-  int my_e = -1;       // lane j keeps slot j's expert and logit
+  int my_e = -1;  // lane j keeps slot j's expert and logit
   float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;  // below every finite key
+    float best = -__builtin_huge_valf();
     int best_i = -1;
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      if (!(taken & (1u << i))) {
-        const uint64_t key = route_key(v[i], lane + 64 * i);
-        if (key > best) { best = key; best_i = i; }
+    for (int i = 0; i < kMaxPer; ++i)
+      if (!(taken & (1u << i)) && (best_i < 0 || v[i] > best)) {
+        best = v[i];
+        best_i = i;
       }
-    }
-    const uint64_t win = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)win);
-    if (best_i >= 0 && best == win) taken |= 1u << best_i;  // unique winner: keys carry the index
+    const float vmax = wave_max_f32(best);
+    const int e = wave_min_i32(best_i >= 0 && best == vmax ? lane + 64 * best_i : INT_MAX);
+    if (lane == (e & 63)) taken |= 1u << (e >> 6);
     if (lane == j) {
       my_e = e;
-      my_v = key_value(win);
+      my_v = vmax;
     }
   }
 
   // softmax over the k selected logits, summed in slot order
-  const float m = __shfl(my_v, 0, 64);
+  const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float ex = (lane < k) ? expf(my_v - m) : 0.0f;
   float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += __shfl(ex, j, 64);
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_e;
     topk_w[(size_t)t * k + lane] = ex / sum;

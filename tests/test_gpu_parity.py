@@ -26,7 +26,17 @@ SMALL = {
                                         seed=13),
     "k1_sparse": moe_synth.make_config("tiny", T=777, d=128, f=256, E_global=64, k=1, e_begin=60, e_end=64,
                                        seed=14),
+    # a steep Zipf prior: most local experts receive no rows, expert 0 two row bands
+    "zipf_empty": moe_synth.make_config("tiny", T=512, d=256, f=128, E_global=32, k=2, e_begin=0, e_end=32,
+                                        zipf_s=3.0, seed=15),
 }
+
+
+def test_zipf_empty_has_empty_and_multi_band_experts():
+    cfg = SMALL["zipf_empty"]
+    ref = oracle.dispatch(*oracle.route_topk(moe_synth.generate(cfg)["logits"].numpy(), cfg.k)[:2],
+                          cfg.e_begin, cfg.e_end, cfg.num_segments)
+    assert (ref["counts"] == 0).sum() >= 8 and ref["counts"].max() > 256
 
 
 def _oracle_and_gpu(cfg, sched="interleaved", **kw):

@@ -146,8 +146,14 @@ __host__ __device__ constexpr int ring_stages(int MB, int NNB, bool FP8) {
 }
 // global -> LDS loads issued per lane per stage (16 bytes each, plus one
 // 4-byte row-scale load with fp8)
+// (band rows: a whole number of instructions per wavefront plus, when they
+// do not divide evenly, one partial instruction in every wavefront)
+__host__ __device__ constexpr int stage_a_rows_per_round(bool FP8) {
+  return gemm_threads(FP8) * 16 / stage_k_bytes(FP8);
+}
 __host__ __device__ constexpr int stage_loads(int MB, int NNB, bool FP8) {
-  return (MB * 32 + NNB * 64) * stage_k_bytes(FP8) / (gemm_threads(FP8) * 16) + (FP8 ? 1 : 0);
+  return (MB * 32 + stage_a_rows_per_round(FP8) - 1) / stage_a_rows_per_round(FP8) +
+         NNB * 64 / stage_a_rows_per_round(FP8) + (FP8 ? 1 : 0);
 }
 
 // Wavefront grid of a tile of width NNB: WM wavefront rows x WN wavefront
@@ -210,18 +216,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int MB, int NNB, bool FP8>
 __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
   constexpr int KB = stage_k_bytes(FP8), CH = KB / 16, RPI = 64 / CH;
-  constexpr int NW = gemm_threads(FP8) / 64;
-  constexpr int NA = MB * 32 / (NW * RPI), NBW = NNB * 64 / (NW * RPI), half = NNB * 32;
-  static_assert(NA * NW * RPI == MB * 32 && NBW * NW * RPI == NNB * 64, "stage rows per wavefront");
+  constexpr int NW = gemm_threads(FP8) / 64, ROUND = NW * RPI;
+  static_assert(ROUND == stage_a_rows_per_round(FP8), "rows per load round");
+  // NAF full rounds of band rows, then REM rows (a multiple of 32) spread over
+  // all wavefronts: REM / NW rows each, the other lanes idle
+  constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
+  constexpr int NBW = NNB * 64 / ROUND, half = NNB * 32;
+  static_assert(NBW * ROUND == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
   const int w = tid >> 6, lane = tid & 63;
   const int kb = kt * KB;
   const int sub = lane / CH, slot = lane % CH;
   if (j < NA) {
-    const int r0 = (j * NW + w) * RPI;
+    constexpr int RPW = REM / NW;  // rows per wavefront in the partial round
+    const bool part = REM && j == NAF;
+    const int r0 = part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI;
     const int r = r0 + sub;
     const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
     const uint8_t* g = t.A + (size_t)gr * t.lda + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
-    __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
+    if (!part || sub < RPW) __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
   } else if (j < NA + NBW) {
     const int r0 = ((j - NA) * NW + w) * RPI;
     const int r = r0 + sub;
@@ -475,23 +487,36 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
   if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc);
 }
 
-// The band's 32-row blocks, rounded up to a multiple MB of the wavefront
-// rows WM so that every wavefront row owns MB / WM blocks and one
-// instantiation serves all wavefronts (rows past the band re-read its last
-// row and are not stored).
+// MB = the band's 32-row blocks. With two wavefront rows (WM = 2) wavefront
+// row 0 owns blocks {0, 2, ...}, i.e. ceil(MB / 2), and row 1 floor(MB / 2),
+// so an odd count costs no MFMAs on absent blocks, and the stage (and with
+// it the ring depth) is sized to the band: three 52 KiB stages of a 160-row
+// band fit in the LDS where 192-row ones would leave two. With four
+// wavefront rows MB is rounded up to a multiple of 4 (rows past the band
+// re-read its last row and are not stored).
 template <int MB, int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
-  static_assert(MB % WaveGrid<NNB, FP8>::WM == 0, "row blocks per wavefront row");
-  tile_body<MB, MB / WaveGrid<NNB, FP8>::WM, NNB, L1, FP8>(P, t, lds);
+  constexpr int WM = WaveGrid<NNB, FP8>::WM;
+  if constexpr (WM == 2 && (MB & 1)) {
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, FP8>(P, t, lds);
+    else tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds);
+  } else {
+    static_assert(MB % WM == 0, "row blocks per wavefront row");
+    tile_body<MB, MB / WM, NNB, L1, FP8>(P, t, lds);
+  }
 }
 
 template <int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
   if constexpr (WaveGrid<NNB, FP8>::WM == 2) {
-    switch ((t.rows + 63) >> 6) {
-      case 1: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
-      case 2: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
-      case 3: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
+    switch ((t.rows + 31) >> 5) {
+      case 1: run_tile<1, NNB, L1, FP8>(P, t, lds); break;
+      case 2: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
+      case 3: run_tile<3, NNB, L1, FP8>(P, t, lds); break;
+      case 4: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
+      case 5: run_tile<5, NNB, L1, FP8>(P, t, lds); break;
+      case 6: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
+      case 7: run_tile<7, NNB, L1, FP8>(P, t, lds); break;
       default: run_tile<8, NNB, L1, FP8>(P, t, lds); break;
     }
   } else {

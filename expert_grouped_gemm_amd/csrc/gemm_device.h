@@ -30,28 +30,33 @@
 //     SwiGLU output it owns. The number of 32-row blocks (rounded up to a
 //     multiple of WM) is a template parameter, so a short band costs fewer
 //     loads and MFMAs;
-//   - in the separate and expert-wave schedules the tile list is walked in
-//     groups of group_m row bands, N-tile by N-tile inside a group, so the
-//     tiles that run at the same time on one XCD share both their row bands
-//     and their weight tiles through that XCD's L2.
+//   - every schedule walks its tile lists in groups of group_m row bands,
+//     N-tile by N-tile inside a group, so the tiles that run at the same time
+//     on one XCD share both their row bands and their weight tiles through
+//     that XCD's L2.
 //
 // Schedules (X-Stage Section 4.2, Algorithm 1, Figure 4):
 //   MODE_SEP_L1/L2    every Linear-1 tile, then (next launch) every Linear-2 tile
 //   MODE_WAVE         experts grouped into waves; a wave's Linear-1 tiles, then
 //                     its Linear-2 tiles; each Linear-2 tile waits on l2_full[p]
 //   MODE_INTERLEAVED  per pair-instance g (two workgroups, roles r = 0, 1) two
-//                     cursors k1, k2 advance by the instance count; a Linear-2
-//                     tile of row p2 = k2 / P2 is emitted only when the Linear-1
-//                     row p1 = k1 / P1 leads it by at least D rows, otherwise
-//                     the next Linear-1 tile; the N-tile of a pair cursor is
-//                     n = 2 (k mod P) + r.
+//                     cursors k1, k2 advance by the instance count over the
+//                     (row band, pair column) lists of Linear-1 and Linear-2,
+//                     both walked in raster groups of group_m bands; a Linear-2
+//                     tile of band p2 is emitted only when the first band of
+//                     the Linear-1 cursor's group leads p2 by at least D bands
+//                     (with group_m = 1: the Linear-1 cursor's band, as in the
+//                     algorithm), otherwise the next Linear-1 tile; the N-tile
+//                     of pair column c is n = 2 c + r.
 // l2_full[p] counts stored Linear-1 tiles of row p (X-Stage Section 4.2,
 // "Condition 2"): the Linear-1 epilogue publishes with an agent-scope release
 // after its H stores, a Linear-2 tile of row p acquires once it reaches the
-// number of Linear-1 tiles per row. A workgroup only waits on rows at least
-// D >= 1 behind its own Linear-1 cursor, so the smallest unfinished Linear-1
-// row always belongs to a workgroup that is not waiting (no deadlock while
-// the whole grid is resident: one workgroup per CU). Waits are bounded; a
+// number of Linear-1 tiles per row. A workgroup only waits on bands that lie
+// in raster groups before its own Linear-1 cursor's group, whose Linear-1
+// tiles all precede its cursor; so the workgroup holding the earliest
+// unfinished Linear-1 tile either runs it or waits on a band that is already
+// complete (no deadlock while the whole grid is resident: one workgroup per
+// CU). Waits are bounded; a
 // timeout sets the sticky error flag meta[META_ERR].
 #pragma once
 
@@ -83,7 +88,7 @@ struct GemmParams {
   int d, f;
   int N1, N2;             // Linear-1 tiles per row band (f / (32 nnb1)), Linear-2 tiles (d / (64 nnb2))
   int nnb1, nnb2;         // tile width (2 or 4) of the Linear-1 and Linear-2 tiles
-  int group_m;            // row bands per raster group (separate and expert-wave schedules)
+  int group_m;            // row bands per raster group of the tile lists
   int mode;
   int lead_D;
   int ready;              // l2_full value at which a row band's H is complete (N1, or f/128 with fp8)
@@ -739,16 +744,22 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
       const int g = lid >> 1, r = lid & 1, Gp = G >> 1;
       const int P1 = (P.N1 + 1) >> 1, P2 = (P.N2 + 1) >> 1;
       const int end1 = Pb * P1, end2 = Pb * P2;
+      const int span1 = P.group_m * P1;
       int k1 = g, k2 = g;
       while (k1 < end1 || k2 < end2) {
-        const int p1 = k1 < end1 ? k1 / P1 : 0x3FFFFFFF;
-        const int p2 = k2 / P2;
-        if (k2 < end2 && p2 + P.lead_D <= p1) {
-          const int n = 2 * (k2 % P2) + r;
+        // first band of k1's raster group: every Linear-1 tile of a lower band
+        // comes before k1 in the Linear-1 order
+        const int b1 = k1 < end1 ? (k1 / span1) * P.group_m : 0x3FFFFFFF;
+        int p2 = 0, c2 = 0;
+        if (k2 < end2) raster(k2, Pb, P2, P.group_m, p2, c2);
+        if (k2 < end2 && p2 + P.lead_D <= b1) {
+          const int n = 2 * c2 + r;
           if (n < P.N2) do_tile<false, FP8>(P, p2, n, true, lds);
           k2 += Gp;
         } else {
-          const int n = 2 * (k1 % P1) + r;
+          int p1, c1;
+          raster(k1, Pb, P1, P.group_m, p1, c1);
+          const int n = 2 * c1 + r;
           if (n < P.N1) do_tile<true, FP8>(P, p1, n, true, lds);
           k1 += Gp;
         }

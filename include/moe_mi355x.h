@@ -93,8 +93,8 @@ enum {
   MOE_FLAG_TILE_NARROW = 1u,      /* every tile 128 weight rows wide */
   MOE_FLAG_TILE_WIDE = 2u,        /* 256 weight rows wide wherever the shape allows (Linear-2 tiles need
                                      d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
-  MOE_FLAG_BAND_MAJOR = 4u        /* walk the separate and expert-wave tile lists row band by row band
-                                     instead of in groups of bands */
+  MOE_FLAG_BAND_MAJOR = 4u        /* walk the expert-GEMM tile lists row band by row band instead of
+                                     in groups of bands */
 };
 
 typedef struct moe_problem {

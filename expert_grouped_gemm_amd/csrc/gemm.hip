@@ -11,7 +11,8 @@ namespace {
 // expert waves (fewest consecutive experts whose Linear-1 tiles reach the grid,
 // or a fixed number of experts per wave).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int N1, int G,
-                                                    int wave_experts, int Pmax, int32_t* __restrict__ blk_done,
+                                                    int wave_experts, int sort_bands, int Pmax,
+                                                    int32_t* __restrict__ blk_done,
                                                     int nblk_done, int32_t* __restrict__ band_expert,
                                                     int32_t* __restrict__ band_row0,
                                                     int32_t* __restrict__ band_rows, int32_t* __restrict__ l2_full,
@@ -54,10 +55,18 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     row_off[El] = offsets[El];
   }
   __syncthreads();
-  // band table, one band per thread: band q belongs to the last expert whose
+  // Band table. Band q (in expert order) belongs to the last expert whose
   // first band is <= q (binary search over start[]; experts without rows have
-  // start[e] == start[e + 1] and are skipped)
-  for (int q = threadIdx.x; q < start[El]; q += blockDim.x) {
+  // start[e] == start[e + 1] and are skipped). With sort_bands the table is
+  // ordered by the band's 32-row blocks, largest first, stably: a static
+  // round-robin over the tiles then gives every workgroup a similar mix of
+  // tile sizes. The order of the bands changes no result, only which tiles
+  // run together.
+  const int Ptot = start[El];
+  __shared__ int cls_base[9];
+  if (threadIdx.x < 9) cls_base[threadIdx.x] = 0;
+  __syncthreads();
+  auto band_of = [&](int q, int& ex, int& r0, int& rows) {
     int lo = 0, hi = El - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -65,12 +74,54 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       else hi = mid - 1;
     }
     const int i = q - start[lo];
-    band_expert[q] = lo;
-    band_row0[q] = row_off[lo] + i * kBM;
-    band_rows[q] = min(kBM, row_off[lo + 1] - row_off[lo] - i * kBM);
+    ex = lo;
+    r0 = row_off[lo] + i * kBM;
+    rows = min(kBM, row_off[lo + 1] - row_off[lo] - i * kBM);
+  };
+  if (sort_bands) {
+    // class c = 8 - blocks (0: a full band); bases = exclusive sums over classes
+    for (int q = threadIdx.x; q < Ptot; q += blockDim.x) {
+      int ex, r0, rows;
+      band_of(q, ex, r0, rows);
+      atomicAdd(&cls_base[8 - ((rows + 31) >> 5)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int s0 = 0;
+      for (int c = 0; c < 9; ++c) { const int v = cls_base[c]; cls_base[c] = s0; s0 += v; }
+    }
+    __syncthreads();
+  }
+  for (int q0 = 0; q0 < Ptot; q0 += blockDim.x) {
+    const int q = q0 + threadIdx.x;
+    int ex = 0, r0 = 0, rows = 0, pos = q;
+    if (q < Ptot) band_of(q, ex, r0, rows);
+    if (sort_bands) {
+      const int cls = q < Ptot ? 8 - ((rows + 31) >> 5) : 9;
+      for (int c = 0; c < 8; ++c) {
+        // stable rank among this chunk's bands of class c
+        const uint64_t bal = __ballot(cls == c);
+        if (lane == 0) sh[wv] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int i = 0; i < 16; ++i) {
+          const int v = sh[i];
+          before += i < wv ? v : 0;
+          total += v;
+        }
+        if (cls == c) pos = cls_base[c] + before + __popcll(bal & ((1ull << lane) - 1ull));
+        __syncthreads();
+        if (threadIdx.x == 0) cls_base[c] += total;
+        __syncthreads();
+      }
+    }
+    if (q < Ptot) {
+      band_expert[pos] = ex;
+      band_row0[pos] = r0;
+      band_rows[pos] = rows;
+    }
   }
   if (threadIdx.x == 0) {
-    const int Ptot = start[El];
     meta[META_P] = Ptot;
     meta[META_A] = offsets[El];
     int nw = 0, tiles = 0, e0 = 0;
@@ -173,7 +224,10 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   }
   P.lead_D = D;
 
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, L.Pmax,
+  // expert waves need expert-contiguous bands; the other schedules take them largest first
+  const int sort_bands = p.sched == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, sort_bands,
+                     L.Pmax,
                      P.blk_done, fp8 ? L.Pmax * (p.f / 128) : 0, reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
                      reinterpret_cast<int32_t*>(ws + L.band_rows), P.l2_full,
                      reinterpret_cast<int32_t*>(ws + L.wave_band0), P.meta);

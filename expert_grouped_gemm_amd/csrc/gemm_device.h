@@ -122,7 +122,8 @@ struct Tile {
   size_t lda, ldb;        // row pitch in bytes
   int rows;               // valid rows of the band (1..256)
   int row0;               // first X_perm / H row of the band
-  int n;                  // N-tile index
+  int n;                  // N-tile index, in units of this tile's width
+  int nnb;                // width: NNB * 64 weight rows
   int ktiles;             // K bytes / stage_k_bytes
   int krot;               // pipeline stage kt streams K slice (kt + krot) mod ktiles
   // fp8 only
@@ -625,7 +626,7 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
   if constexpr (!FP8) {
     if (fused) publish(P.l2_full + p, 1);
   } else {
-    const int bn1 = P.nnb1 * 32;
+    const int bn1 = t.nnb * 32;
     const int j = (t.n * bn1) >> 7;
     const int need = 128 / bn1;
     __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)lds;
@@ -642,15 +643,15 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
 }
 
 template <bool L1, bool FP8>
-__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, bool fused, lds_t* lds) {
+__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int nnb, bool fused, lds_t* lds) {
   constexpr int esz = FP8 ? 1 : 2;
   Tile t;
   const int e = P.band_expert[p];
   t.row0 = P.band_row0[p];
   t.rows = P.band_rows[p];
   t.n = n;
+  t.nnb = nnb;
   t.cap_stride = P.cap;
-  const int nnb = L1 ? P.nnb1 : P.nnb2;
   if constexpr (L1) {
     const int bn = nnb * 32;  // SwiGLU columns: bn gate rows and bn up rows
     t.lda = (size_t)P.d * esz;
@@ -701,6 +702,31 @@ __device__ __forceinline__ void raster(int i, int nb, int N, int gm, int& p, int
   n = j / rows;
 }
 
+// One launch of the separate schedule: every tile of one Linear over nb row
+// bands x N tiles of width nnb, in raster order. When the tiles are wide and
+// the last round of the persistent grid would be partly idle (a tail of
+// fewer than G tiles), that tail runs as twice as many half-width tiles:
+// wide tile n of a band is exactly narrow tiles 2n and 2n+1, with the same K
+// order, so the last round keeps every workgroup busy for half as long.
+template <bool L1, bool FP8>
+__device__ __forceinline__ void separate_tiles(const GemmParams& P, int nb, int N, int nnb, int lid, int G,
+                                               lds_t* lds) {
+  const int total = nb * N;
+  const int cut = (nnb == 4 && total % G) ? total / G * G : total;
+  const int end = cut + 2 * (total - cut);
+  int p, n;
+  for (int i = lid; i < end; i += G) {
+    if (i < cut) {
+      raster(i, nb, N, P.group_m, p, n);
+      do_tile<L1, FP8>(P, p, n, nnb, false, lds);
+    } else {
+      const int j = i - cut;
+      raster(cut + (j >> 1), nb, N, P.group_m, p, n);
+      do_tile<L1, FP8>(P, p, 2 * n + (j & 1), 2, false, lds);
+    }
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
@@ -714,16 +740,10 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
   int p, n;
   switch (P.mode) {
     case MODE_SEP_L1:
-      for (int i = lid; i < Pb * P.N1; i += G) {
-        raster(i, Pb, P.N1, P.group_m, p, n);
-        do_tile<true, FP8>(P, p, n, false, lds);
-      }
+      separate_tiles<true, FP8>(P, Pb, P.N1, P.nnb1, lid, G, lds);
       break;
     case MODE_SEP_L2:
-      for (int i = lid; i < Pb * P.N2; i += G) {
-        raster(i, Pb, P.N2, P.group_m, p, n);
-        do_tile<false, FP8>(P, p, n, false, lds);
-      }
+      separate_tiles<false, FP8>(P, Pb, P.N2, P.nnb2, lid, G, lds);
       break;
     case MODE_WAVE: {
       const int nw = P.meta[META_NWAVES];
@@ -731,11 +751,11 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
         const int pb0 = P.wave_band0[wv], pb1 = P.wave_band0[wv + 1];
         for (int i = lid; i < (pb1 - pb0) * P.N1; i += G) {
           raster(i, pb1 - pb0, P.N1, P.group_m, p, n);
-          do_tile<true, FP8>(P, pb0 + p, n, true, lds);
+          do_tile<true, FP8>(P, pb0 + p, n, P.nnb1, true, lds);
         }
         for (int i = lid; i < (pb1 - pb0) * P.N2; i += G) {
           raster(i, pb1 - pb0, P.N2, P.group_m, p, n);
-          do_tile<false, FP8>(P, pb0 + p, n, true, lds);
+          do_tile<false, FP8>(P, pb0 + p, n, P.nnb2, true, lds);
         }
       }
       break;
@@ -754,13 +774,13 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
         if (k2 < end2) raster(k2, Pb, P2, P.group_m, p2, c2);
         if (k2 < end2 && p2 + P.lead_D <= b1) {
           const int n = 2 * c2 + r;
-          if (n < P.N2) do_tile<false, FP8>(P, p2, n, true, lds);
+          if (n < P.N2) do_tile<false, FP8>(P, p2, n, P.nnb2, true, lds);
           k2 += Gp;
         } else {
           int p1, c1;
           raster(k1, Pb, P1, P.group_m, p1, c1);
           const int n = 2 * c1 + r;
-          if (n < P.N1) do_tile<true, FP8>(P, p1, n, true, lds);
+          if (n < P.N1) do_tile<true, FP8>(P, p1, n, P.nnb1, true, lds);
           k1 += Gp;
         }
       }

@@ -97,23 +97,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     int ex = 0, r0 = 0, rows = 0, pos = q;
     if (q < Ptot) band_of(q, ex, r0, rows);
     if (sort_bands) {
+      // stable rank among this chunk's bands of the same class: a ballot per
+      // class in every wavefront, the per-wavefront counts exchanged once
+      __shared__ int wave_cls[16][8];
       const int cls = q < Ptot ? 8 - ((rows + 31) >> 5) : 9;
+      uint64_t mine = 0;
+#pragma unroll
       for (int c = 0; c < 8; ++c) {
-        // stable rank among this chunk's bands of class c
         const uint64_t bal = __ballot(cls == c);
-        if (lane == 0) sh[wv] = __popcll(bal);
-        __syncthreads();
-        int before = 0, total = 0;
-        for (int i = 0; i < 16; ++i) {
-          const int v = sh[i];
-          before += i < wv ? v : 0;
-          total += v;
-        }
-        if (cls == c) pos = cls_base[c] + before + __popcll(bal & ((1ull << lane) - 1ull));
-        __syncthreads();
-        if (threadIdx.x == 0) cls_base[c] += total;
-        __syncthreads();
+        if (lane == c) wave_cls[wv][c] = __popcll(bal);
+        if (cls == c) mine = bal;
       }
+      __syncthreads();
+      if (cls < 8) {
+        int before = 0;
+        for (int i = 0; i < wv; ++i) before += wave_cls[i][cls];
+        pos = cls_base[cls] + before + __popcll(mine & ((1ull << lane) - 1ull));
+      }
+      __syncthreads();
+      if (threadIdx.x < 8) {
+        int total = 0;
+        for (int i = 0; i < 16; ++i) total += wave_cls[i][threadIdx.x];
+        cls_base[threadIdx.x] += total;
+      }
+      __syncthreads();
     }
     if (q < Ptot) {
       band_expert[pos] = ex;

@@ -113,6 +113,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 
 struct Tile {
@@ -141,11 +142,12 @@ __host__ __device__ constexpr int stage_k_bytes(bool) { return 128; }
 
 // LDS ring geometry per number of 32-row blocks MB and tile width NNB: a stage
 // holds MB*32 rows of the band plus the NNB*64 weight rows, stage_k_bytes of K
-// each; with fp8 also the 256 row scales of the stage's K block (1 KiB).
+// each; with fp8 also the 256 row scales of the stage's K block (1 KiB) and
+// the block's two weight scales (padded to 16 bytes).
 __host__ __device__ constexpr int stage_a_bytes(int MB, bool FP8) { return MB * 32 * stage_k_bytes(FP8); }
 __host__ __device__ constexpr int stage_b_bytes(int NNB, bool FP8) { return NNB * 64 * stage_k_bytes(FP8); }
 __host__ __device__ constexpr int stage_bytes(int MB, int NNB, bool FP8) {
-  return stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + (FP8 ? kBM * 4 : 0);
+  return stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + (FP8 ? kBM * 4 + 16 : 0);
 }
 __host__ __device__ constexpr int ring_stages(int MB, int NNB, bool FP8) {
   return kGemmLds / stage_bytes(MB, NNB, FP8) > 8 ? 8 : kGemmLds / stage_bytes(MB, NNB, FP8);
@@ -159,7 +161,7 @@ __host__ __device__ constexpr int stage_a_rows_per_round(bool FP8) {
 }
 __host__ __device__ constexpr int stage_loads(int MB, int NNB, bool FP8) {
   return (MB * 32 + stage_a_rows_per_round(FP8) - 1) / stage_a_rows_per_round(FP8) +
-         NNB * 64 / stage_a_rows_per_round(FP8) + (FP8 ? 1 : 0);
+         NNB * 64 / stage_a_rows_per_round(FP8) + (FP8 ? 2 : 0);
 }
 
 // Wavefront grid of a tile of width NNB: WM wavefront rows x WN wavefront
@@ -212,7 +214,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One pipeline stage: K bytes [kt*KB, kt*KB+KB) of the band's first 32*MB
 // rows and of the tile's NNB*64 weight rows (and, with fp8, the 256 row scales
-// of K block kt), in stage_loads(MB, NNB, FP8) load instructions per lane:
+// of K block kt and the block's two weight scales), in stage_loads(MB, NNB,
+// FP8) load instructions per lane:
 // first the band rows, then the weight rows, then the scales. Lane i of a
 // 16-byte instruction lands at LDS base + 16*i (64/CH rows of KB bytes, CH =
 // KB/16 chunks per row), lane i of a 4-byte instruction at base + 4*i.
@@ -247,13 +250,22 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
     const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
     __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + r0 * KB, 16, 0, 0);
   } else if constexpr (FP8) {
-    // the 256 row scales: kBM / NW per wavefront, one 4-byte lane each
-    constexpr int PER = kBM / NW;
-    const int r = w * PER + lane;
-    const int gr = r < t.rows ? r : t.rows - 1;
-    const float* g = t.As + (size_t)kt * t.cap_stride + gr;
-    if (lane < PER)
-      __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + w * PER * 4, 4, 0, 0);
+    lds_t* ss = st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8);
+    if (j == NA + NBW) {
+      // the 256 row scales: kBM / NW per wavefront, one 4-byte lane each
+      constexpr int PER = kBM / NW;
+      const int r = w * PER + lane;
+      const int gr = r < t.rows ? r : t.rows - 1;
+      const float* g = t.As + (size_t)kt * t.cap_stride + gr;
+      if (lane < PER) __builtin_amdgcn_global_load_lds(g, ss + w * PER * 4, 4, 0, 0);
+    } else {
+      // the block's two weight scales (first and second half of the weight
+      // rows) after the row scales. Every wavefront loads them, the same 8
+      // bytes, so that all wavefronts issue the same number of loads per
+      // stage; kept in the stage, they need no scalar load in the MFMA loop.
+      const float* g = lane == 0 ? t.Sg + kt : t.Su + kt;
+      if (lane < 2) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4, 4, 0, 0);
+    }
   }
 }
 
@@ -363,25 +375,14 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
   }
 }
 
-// Load p[i] where p and i are the same in every lane, through the scalar
-// cache (a read-only weight scale): a vector load here would be counted by
-// vmcnt and force a wait that drains the global->LDS prefetch ring.
-__device__ __forceinline__ float uniform_load(const float* p, int i) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p + i);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return *reinterpret_cast<const __attribute__((address_space(4))) float*>(((uint64_t)hi << 32) | lo);
-}
-
 template <int MB, int NMB, int NNB, bool FP8>
 __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int tid,
                                             f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
   if constexpr (FP8) {
-    const int ks = kslice(t, kt);
-    const float swg = uniform_load(t.Sg, ks), swu = uniform_load(t.Su, ks);
     static_assert(stage_k_bytes(true) == 128, "an fp8 stage is one 128-wide scale block");
-    compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8),
-                                swg, swu, tid, acc);
+    const lds_t* ss = st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8);
+    const float swg = *(const lds_f32*)(ss + kBM * 4), swu = *(const lds_f32*)(ss + kBM * 4 + 4);
+    compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), ss, swg, swu, tid, acc);
   } else {
     compute_stage<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), tid, acc);
   }

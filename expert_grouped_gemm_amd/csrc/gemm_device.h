@@ -341,12 +341,6 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
   using G = WaveGrid<NNB, true>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
-  i32x8 b[2][G::NCB];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int nb = 0; nb < G::NCB; ++nb)
-      b[ks][nb] = lds_read_32B(sb, wave_col<NNB, true>(nb / G::CPH, nb % G::CPH, wn, lr), ks * 4 + hi * 2);
   const f32x16 zero = {};
 #pragma unroll
   for (int mi = 0; mi < NMB; ++mi) {
@@ -356,9 +350,12 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
     for (int ks = 0; ks < 2; ++ks) {
       const i32x8 a = lds_read_32B(sa, mb * 32 + lr, ks * 4 + hi * 2);
 #pragma unroll
-      for (int nb = 0; nb < G::NCB; ++nb)
-        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[ks][nb], ks ? part[nb] : zero, 0, 0, 0,
-                                                                   127, 0, 127);
+      for (int nb = 0; nb < G::NCB; ++nb) {
+        // weight fragments are read per row block, not kept: with two
+        // wavefronts per SIMD a wavefront has 256 registers
+        const i32x8 b = lds_read_32B(sb, wave_col<NNB, true>(nb / G::CPH, nb % G::CPH, wn, lr), ks * 4 + hi * 2);
+        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, ks ? part[nb] : zero, 0, 0, 0, 127, 0, 127);
+      }
     }
     // the lane's rows of block mb: mb*32 + 8*g + 4*hi + (0..3), g = 0..3
 #pragma unroll

@@ -43,6 +43,8 @@ def parse():
                     help="expert-GEMM tile width (default: chosen from the shape)")
     ap.add_argument("--band-major", action="store_true", help="no grouped raster of the GEMM tile lists")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", action="store_true",
+                    help="after the timed steps, run one call with per-tile timing and summarise the spans")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy (HBM reference and counter calibration)")
@@ -92,6 +94,46 @@ def measured_traffic(cfg, sched, tiles="auto", band_major=False):
     if blob.get("gemm_source_sha256_16") != digest or blob.get("tiles", "auto") != tiles or band_major:
         return None
     return blob.get("hbm_bytes_per_launch")
+
+
+def trace_summary(moe, cfg, args, g, v):
+    """One expert-GEMM call (outside the timed steps) with per-tile timing:
+    per tile kind the mean readiness wait, K-loop and epilogue spans; the
+    share of the workgroups' busy time spent in epilogues, which nothing in
+    the same workgroup overlaps (the exposed stall of X-Stage Eq. 15 with an
+    empty cover window); and how long workgroups sit idle at the end."""
+    import numpy as np
+    import torch
+    p = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
+                         num_segments=cfg.num_segments, sched=args.sched, lead_D=args.lead_D,
+                         quant_block=cfg.quant_block, tiles=args.tiles, band_major=args.band_major, trace=True)
+    ws = moe.alloc_workspace(p)
+    # the dispatch outputs of the timed steps stand for this call's
+    v2 = moe.workspace_views(p, ws)
+    for key in ("offsets", "row_dst"):
+        v2[key].copy_(v[key])
+    moe.expert_forward(p, v["x_perm"], v.get("x_perm_scale"), v2["offsets"], v2["row_dst"], g["W1"],
+                       g.get("W1_scale"), g["W2"], g.get("W2_scale"), v2["combine_buf"], ws)
+    torch.cuda.synchronize()
+    moe.check_workspace(p, ws)
+    tr = moe.tile_trace(p, ws)
+    t0, t1 = float(tr["t_start"].min()), float(tr["t_end"].max())
+    span = t1 - t0
+    busy = tr["t_end"] - tr["t_start"]
+    wgs = np.unique(tr["wg"])
+    last = np.array([tr["t_end"][tr["wg"] == w].max() for w in wgs])
+    res = {"clock_hz": moe.lib().moe_tile_clock_hz(), "tiles": int(busy.size), "workgroups": int(wgs.size),
+           "makespan_us": round(span, 2),
+           "busy_frac": round(float(busy.sum()) / (wgs.size * span), 4),
+           "epilogue_share": round(float((tr["t_end"] - tr["t_main_end"]).sum() / busy.sum()), 4),
+           "tail_idle_us_mean": round(float((t1 - last).mean()), 2)}
+    for k, name in ((1, "linear1"), (2, "linear2")):
+        m = tr["kind"] == k
+        res[name] = {"tiles": int(m.sum()),
+                     "wait_us_mean": round(float((tr["t_ready"] - tr["t_start"])[m].mean()), 3),
+                     "mainloop_us_mean": round(float((tr["t_main_end"] - tr["t_ready"])[m].mean()), 3),
+                     "epilogue_us_mean": round(float((tr["t_end"] - tr["t_main_end"])[m].mean()), 3)}
+    return res
 
 
 def main():
@@ -217,6 +259,9 @@ def main():
             "avg_launch_us": round(gemm_us, 2),
         },
     }
+
+    if args.trace:
+        out["tile_trace"] = trace_summary(moe, cfg, args, g, v)
 
     if args.copy_probe:
         n = 1 << 30

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
     "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
-    "check_workspace", "SCHED", "DTYPE", "STATUS",
+    "check_workspace", "tile_trace", "SCHED", "DTYPE", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ DTYPE = {"bf16": 0, "fp8_e4m3": 1}
 # MOE_FLAG_* of moe_mi355x.h
 TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
 FLAG_BAND_MAJOR = 4
+FLAG_TILE_TRACE = 8
 
 
 class MoEError(RuntimeError):
@@ -55,7 +56,8 @@ class Problem(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_idx", "topk_w", "counts", "offsets", "row_src", "row_dst", "tok_off", "comb_w", "x_perm",
-        "x_perm_scale", "h", "h_scale", "h_f32", "combine_buf", "meta", "total")]
+        "x_perm_scale", "h", "h_scale", "h_f32", "combine_buf", "meta", "tile_trace", "tile_trace_capacity",
+        "total")]
 
 
 _lib = None
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.moe_check_workspace.restype = ctypes.c_int
         L.moe_check_workspace.argtypes = [PP, _P, ctypes.c_size_t, _P]
+        L.moe_tile_clock_hz.restype = ctypes.c_double
+        L.moe_tile_clock_hz.argtypes = []
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_last_hip_error.restype = ctypes.c_int
@@ -99,10 +103,11 @@ def lib() -> ctypes.CDLL:
 def make_problem(T: int, d: int, f: int, E_global: int, k: int, e_begin: int = 0, e_end: Optional[int] = None,
                  dtype: str = "bf16", num_segments: int = 1, sched: str = "interleaved", lead_D: int = 0,
                  wave_experts: int = 0, grid: int = 0, quant_block: int = 128, tiles: str = "auto",
-                 band_major: bool = False) -> Problem:
+                 band_major: bool = False, trace: bool = False) -> Problem:
     """tiles: "auto" (chosen from the shape), "narrow" or "wide" expert-GEMM tiles;
-    band_major: walk the separate / expert-wave tile lists band by band."""
-    flags = TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0)
+    band_major: walk the separate / expert-wave tile lists band by band;
+    trace: record one timed span per expert-GEMM tile (read with tile_trace)."""
+    flags = TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0) | (FLAG_TILE_TRACE if trace else 0)
     return Problem(T=T, d=d, f=f, E_global=E_global, k=k, e_begin=e_begin,
                    e_end=E_global if e_end is None else e_end, dtype=DTYPE[dtype], quant_block=quant_block,
                    num_segments=num_segments, sched=SCHED[sched], lead_D=lead_D, wave_experts=wave_experts,
@@ -179,7 +184,36 @@ def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
         v["x_perm_scale"] = view(L.x_perm_scale, cap * (p.d // 128), torch.float32, (p.d // 128, cap))
         v["h_scale"] = view(L.h_scale, cap * (p.f // 128), torch.float32, (p.f // 128, cap))
         v["h_f32"] = view(L.h_f32, cap * p.f, torch.float32, (cap, p.f))
+    if L.tile_trace_capacity:
+        v["tile_trace"] = view(L.tile_trace, L.tile_trace_capacity * 5, torch.int64, (L.tile_trace_capacity, 5))
     return v
+
+
+def tile_trace(p: Problem, ws: torch.Tensor) -> Dict[str, "np.ndarray"]:
+    """The expert-GEMM tile records of the last call on `ws` (a problem made with
+    trace=True), decoded: clock readings t_start, t_ready, t_main_end, t_end in
+    microseconds from the earliest start, and kind (1 = Linear-1, 2 = Linear-2),
+    nnb (tile width in 32-row weight blocks per half), wg (workgroup), n (tile
+    index in units of its width) and band (row band) per tile."""
+    import numpy as np
+    v = workspace_views(p, ws)
+    if "tile_trace" not in v:
+        raise ValueError("tile_trace: the problem was made without trace=True")
+    count = int(v["meta"][4])
+    cap = v["tile_trace"].shape[0]
+    if count > cap:
+        raise RuntimeError(f"tile_trace: {count} tile records for a region of {cap}")
+    hz = lib().moe_tile_clock_hz()
+    if hz <= 0:
+        raise RuntimeError("tile_trace: the device does not report its wall-clock rate")
+    r = v["tile_trace"][:count].cpu().numpy().view(np.uint64)
+    t0 = int(r[:, 0].min()) if count else 0
+    us = lambda c: (r[:, c].astype(np.int64) - t0) / hz * 1e6
+    info = r[:, 4]
+    return dict(t_start=us(0), t_ready=us(1), t_main_end=us(2), t_end=us(3),
+                kind=(info & 3).astype(np.int64), nnb=((info >> 2) & 7).astype(np.int64),
+                wg=((info >> 8) & 0xFFFF).astype(np.int64), n=((info >> 24) & 0xFFFF).astype(np.int64),
+                band=(info >> 40).astype(np.int64))
 
 
 def route_topk(p: Problem, logits, topk_idx, topk_w, counts_global=None, stream=None):

@@ -21,7 +21,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   __shared__ int sh[64];
   for (int i = threadIdx.x; i < Pmax; i += blockDim.x) l2_full[i] = 0;
   for (int i = threadIdx.x; i < nblk_done; i += blockDim.x) blk_done[i] = 0;
-  if (threadIdx.x == 0) meta[META_ERR] = 0;  // the flag reports this call only
+  if (threadIdx.x == 0) {
+    meta[META_ERR] = 0;  // the flag reports this call only
+    meta[META_TRACE_N] = 0;
+  }
   const int e = threadIdx.x;
   int cnt = 0, nb = 0;
   if (e < El) {
@@ -219,6 +222,8 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.N2 = p.d / (64 * tc.nnb2);
   P.ready = fp8 ? p.f / 128 : P.N1;
   P.blk_done = reinterpret_cast<int32_t*>(ws + L.blk_done);
+  P.trace = L.pub.tile_trace_capacity ? reinterpret_cast<uint64_t*>(ws + L.pub.tile_trace) : nullptr;
+  P.trace_cap = (int)L.pub.tile_trace_capacity;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile (128), K the participating workgroups and h = f,
   // i.e. the rows one sweep of the grid covers. The knee is a lower bound;

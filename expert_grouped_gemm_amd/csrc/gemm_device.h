@@ -92,6 +92,8 @@ struct GemmParams {
   int mode;
   int lead_D;
   int ready;              // l2_full value at which a row band's H is complete (N1, or f/128 with fp8)
+  uint64_t* trace;        // tile records of 5 words (moe_tile_record_t), or null: no timing
+  int trace_cap;          // records the trace region holds
 };
 
 // Launch the persistent expert-GEMM kernel of one operand type (bf16 in
@@ -446,7 +448,7 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
 template <int MB, int NMB, int NNB, bool L1, bool FP8>
-__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds) {
+__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8), LD = stage_loads(MB, NNB, FP8);
@@ -488,6 +490,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
     drain<MB, NMB, NNB, FP8, S - 2>(t, lds, rd, kt, tid, acc);
   }
   lds_barrier();  // LDS ring free for the next tile
+  if (P.trace) t_main = __builtin_amdgcn_s_memrealtime();
   if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc);
 }
 
@@ -499,34 +502,34 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
 // wavefront rows MB is rounded up to a multiple of 4 (rows past the band
 // re-read its last row and are not stored).
 template <int MB, int NNB, bool L1, bool FP8>
-__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
   constexpr int WM = WaveGrid<NNB, FP8>::WM;
   if constexpr (WM == 2 && (MB & 1)) {
-    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, FP8>(P, t, lds);
-    else tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds);
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, FP8>(P, t, lds, t_main);
+    else tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds, t_main);
   } else {
     static_assert(MB % WM == 0, "row blocks per wavefront row");
-    tile_body<MB, MB / WM, NNB, L1, FP8>(P, t, lds);
+    tile_body<MB, MB / WM, NNB, L1, FP8>(P, t, lds, t_main);
   }
 }
 
 template <int NNB, bool L1, bool FP8>
-__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds) {
+__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
   if constexpr (WaveGrid<NNB, FP8>::WM == 2) {
     switch ((t.rows + 31) >> 5) {
-      case 1: run_tile<1, NNB, L1, FP8>(P, t, lds); break;
-      case 2: run_tile<2, NNB, L1, FP8>(P, t, lds); break;
-      case 3: run_tile<3, NNB, L1, FP8>(P, t, lds); break;
-      case 4: run_tile<4, NNB, L1, FP8>(P, t, lds); break;
-      case 5: run_tile<5, NNB, L1, FP8>(P, t, lds); break;
-      case 6: run_tile<6, NNB, L1, FP8>(P, t, lds); break;
-      case 7: run_tile<7, NNB, L1, FP8>(P, t, lds); break;
-      default: run_tile<8, NNB, L1, FP8>(P, t, lds); break;
+      case 1: run_tile<1, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 2: run_tile<2, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 3: run_tile<3, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 4: run_tile<4, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 5: run_tile<5, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 6: run_tile<6, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 7: run_tile<7, NNB, L1, FP8>(P, t, lds, t_main); break;
+      default: run_tile<8, NNB, L1, FP8>(P, t, lds, t_main); break;
     }
   } else {
     static_assert(WaveGrid<NNB, FP8>::WM == 4, "wavefront rows");
-    if (t.rows <= 128) run_tile<4, NNB, L1, FP8>(P, t, lds);
-    else run_tile<8, NNB, L1, FP8>(P, t, lds);
+    if (t.rows <= 128) run_tile<4, NNB, L1, FP8>(P, t, lds, t_main);
+    else run_tile<8, NNB, L1, FP8>(P, t, lds, t_main);
   }
 }
 
@@ -615,10 +618,14 @@ __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
 
 // After a Linear-1 tile's stores. bf16 (fused schedules only): count the tile
 // in l2_full[p]; the band is ready at N1. fp8: the 128-column block j is
-// covered by 128 / (32 nnb1) tiles (2 narrow, 1 wide); each counts itself in
-// blk_done[p][j], and the last of them (every one of the block's Hf stores is
-// then published) quantises the block and counts it in l2_full[p]; the band
-// is ready at f / 128.
+// covered by 128 / (32 nnb1) tiles (2 narrow, 1 wide). A wide tile quantises
+// its own block as soon as its workgroup's Hf stores are done (each wave
+// waits for its stores, then the barrier: no other CU wrote or read those
+// lines, so nothing needs a device-scope release or a cache write-back). Narrow tiles each count themselves in blk_done[p][j] at
+// device scope, and the second (every Hf store of the block is then
+// published) quantises it. In the fused schedules the quantised block is
+// counted in l2_full[p]; the band is ready at f / 128. The separate schedule
+// needs no counting for Linear-2: its launch starts after this one ends.
 template <bool FP8>
 __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& t, int p, bool fused, lds_t* lds) {
   if constexpr (!FP8) {
@@ -627,6 +634,13 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
     const int bn1 = t.nnb * 32;
     const int j = (t.n * bn1) >> 7;
     const int need = 128 / bn1;
+    if (need == 1) {
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's Hf stores are done
+      __syncthreads();
+      quantize_block(P, t.row0, t.rows, j);
+      if (fused) publish(P.l2_full + p, 1);
+      return;
+    }
     __attribute__((address_space(3))) int* flag = (__attribute__((address_space(3))) int*)lds;
     const int old = publish(P.blk_done + (size_t)p * (P.f >> 7) + j, 1);
     if (threadIdx.x == 0) *flag = old;
@@ -635,7 +649,31 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
     __syncthreads();  // the ring (and the flag in it) is reused by the next tile
     if (second) {
       quantize_block(P, t.row0, t.rows, j);
-      publish(P.l2_full + p, 1);
+      if (fused) publish(P.l2_full + p, 1);
+    }
+  }
+}
+
+// Tile timing (P.trace set): once every wavefront's epilogue stores (and
+// publication) are done, thread 0 takes a record slot from the device-scope
+// counter meta[META_TRACE_N] and writes the tile's four clock readings and
+// its identity. The extra barrier makes t_end the time the whole tile left
+// the CU.
+__device__ __forceinline__ void record_tile(const GemmParams& P, bool l1, int p, int n, int nnb, uint64_t t_start,
+                                            uint64_t t_ready, uint64_t t_main) {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    const int slot = __hip_atomic_fetch_add(P.meta + META_TRACE_N, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (slot < P.trace_cap) {
+      uint64_t* r = P.trace + (size_t)slot * 5;
+      r[0] = t_start;
+      r[1] = t_ready;
+      r[2] = t_main;
+      r[3] = t_end;
+      r[4] = (uint64_t)(l1 ? 1 : 2) | ((uint64_t)nnb << 2) | ((uint64_t)blockIdx.x << 8) | ((uint64_t)n << 24) |
+             ((uint64_t)p << 40);
     }
   }
 }
@@ -643,6 +681,8 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
 template <bool L1, bool FP8>
 __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int nnb, bool fused, lds_t* lds) {
   constexpr int esz = FP8 ? 1 : 2;
+  uint64_t t_start = 0, t_ready = 0, t_main = 0;
+  if (P.trace) t_start = __builtin_amdgcn_s_memrealtime();
   Tile t;
   const int e = P.band_expert[p];
   t.row0 = P.band_row0[p];
@@ -682,9 +722,11 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
     }
     if (fused) wait_row_ready(P, p);
   }
-  if (nnb == 4) dispatch_tile<4, L1, FP8>(P, t, lds);
-  else dispatch_tile<2, L1, FP8>(P, t, lds);
+  if (P.trace) t_ready = __builtin_amdgcn_s_memrealtime();
+  if (nnb == 4) dispatch_tile<4, L1, FP8>(P, t, lds, t_main);
+  else dispatch_tile<2, L1, FP8>(P, t, lds, t_main);
   if constexpr (L1) finish_l1_tile<FP8>(P, t, p, fused, lds);
+  if (P.trace) record_tile(P, L1, p, n, nnb, t_start, t_ready, t_main);
 }
 
 // Tile i of a list of nb row bands x N tiles, walked in groups of gm bands:

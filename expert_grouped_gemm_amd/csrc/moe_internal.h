@@ -22,7 +22,7 @@ constexpr int gemm_threads(bool) { return 512; }
 constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
 constexpr int kMetaInts = 64;
-enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3 };
+enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4 };
 
 enum GemmMode { MODE_SEP_L1 = 0, MODE_SEP_L2 = 1, MODE_WAVE = 2, MODE_INTERLEAVED = 3 };
 
@@ -95,6 +95,11 @@ inline Layout make_layout(const moe_problem_t& p) {
   L.pub.h_scale = take(fp8 ? cap * (p.f / 128) * 4 : 0);
   L.pub.combine_buf = take(cap * p.d * 4);
   L.pub.h_f32 = take(fp8 ? cap * p.f * 4 : 0);
+  // a bound on the tiles of one call: every band at the narrow widths
+  // (f / 64 Linear-1 tiles and d / 128 Linear-2 tiles)
+  L.pub.tile_trace_capacity =
+      (p.flags & MOE_FLAG_TILE_TRACE) ? (size_t)L.Pmax * (size_t)(p.f / 64 + p.d / 128) : 0;
+  L.pub.tile_trace = take(L.pub.tile_trace_capacity * sizeof(moe_tile_record_t));
   L.pub.total = o;
   return L;
 }

@@ -93,9 +93,29 @@ enum {
   MOE_FLAG_TILE_NARROW = 1u,      /* every tile 128 weight rows wide */
   MOE_FLAG_TILE_WIDE = 2u,        /* 256 weight rows wide wherever the shape allows (Linear-2 tiles need
                                      d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
-  MOE_FLAG_BAND_MAJOR = 4u        /* walk the expert-GEMM tile lists row band by row band instead of
+  MOE_FLAG_BAND_MAJOR = 4u,       /* walk the expert-GEMM tile lists row band by row band instead of
                                      in groups of bands */
+  MOE_FLAG_TILE_TRACE = 8u        /* record one span per expert-GEMM tile in the workspace region
+                                     tile_trace (moe_tile_record_t); costs a few clock reads per tile */
 };
+
+/* One expert-GEMM tile as recorded with MOE_FLAG_TILE_TRACE: the per-tile
+ * spans that X-Stage, Section 5.2.3, measures to test its Eq. 15 (mainloop
+ * against epilogue stores). Times are reads of the device-wide constant-rate
+ * clock (s_memrealtime; its rate is moe_tile_clock_hz()):
+ * t_start when the workgroup takes the tile, t_ready once its inputs are
+ * ready (a Linear-2 tile of a fused schedule first waits for its row band's
+ * Linear-1 tiles), t_main_end after the K loop, t_end after the epilogue
+ * stores (and, for Linear-1 in the fused schedules or fp8, after publishing
+ * them). info packs kind (bits 0-1: 1 = Linear-1, 2 = Linear-2), the tile
+ * width NNB (bits 2-4; 128 or 256 weight rows for 2 or 4), the workgroup
+ * (bits 8-23), the N-tile index in units of its width (bits 24-39) and the row
+ * band (bits 40-63). The region holds tile_trace_capacity records; the
+ * number written is meta[4] (records past the capacity are dropped). */
+typedef struct moe_tile_record {
+  uint64_t t_start, t_ready, t_main_end, t_end;
+  uint64_t info;
+} moe_tile_record_t;
 
 typedef struct moe_problem {
   int32_t T;             /* tokens */
@@ -135,7 +155,10 @@ typedef struct moe_workspace_layout {
   size_t h_f32;         /* fp32  [cap, f]   fp8 only: SwiGLU output before its e4m3 quantisation */
   size_t combine_buf;   /* fp32  [cap, d]   Linear-2 output in token-order slots */
   size_t meta;          /* int32 [64]       meta[0] = A (local assignments), meta[1] = row bands,
-                                            meta[2] = error flag of the last call (1 = wait timed out) */
+                                            meta[2] = error flag of the last call (1 = wait timed out),
+                                            meta[4] = tile records written (MOE_FLAG_TILE_TRACE) */
+  size_t tile_trace;    /* moe_tile_record_t [tile_trace_capacity]; empty without MOE_FLAG_TILE_TRACE */
+  size_t tile_trace_capacity;  /* records (a bound on the tiles of one call) */
   size_t total;         /* = moe_workspace_size */
 } moe_workspace_layout_t;
 
@@ -201,6 +224,9 @@ MOE_API const char* moe_status_string(moe_status_t s);
 MOE_API int moe_last_hip_error(void);
 /* Library version, e.g. "0.1.0". */
 MOE_API const char* moe_version(void);
+/* Frequency in Hz of the clock the moe_tile_record_t readings count (the
+ * current device's constant-rate wall clock), or 0 if HIP cannot report it. */
+MOE_API double moe_tile_clock_hz(void);
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(moe.Problem) == 15 * 4
-    assert ctypes.sizeof(moe.WorkspaceLayout) == 16 * 8
+    assert ctypes.sizeof(moe.WorkspaceLayout) == 18 * 8
 
 
 GOOD = dict(T=64, d=128, f=256, E_global=4, k=2)
@@ -66,7 +66,7 @@ def test_unsupported_shapes(L, over, code):
 
 
 def test_invalid_enums_and_flags(L):
-    for field, val in (("dtype", 7), ("sched", 3), ("flags", 3), ("flags", 8), ("lead_D", -1), ("grid", -2)):
+    for field, val in (("dtype", 7), ("sched", 3), ("flags", 3), ("flags", 16), ("lead_D", -1), ("grid", -2)):
         p = moe.make_problem(**GOOD)
         setattr(p, field, val)
         out = moe.WorkspaceLayout()

@@ -225,14 +225,21 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.trace = L.pub.tile_trace_capacity ? reinterpret_cast<uint64_t*>(ws + L.pub.tile_trace) : nullptr;
   P.trace_cap = (int)L.pub.tile_trace_capacity;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
-  // rows of a Linear-1 tile (128), K the participating workgroups and h = f,
-  // i.e. the rows one sweep of the grid covers. The knee is a lower bound;
-  // below 8 rows Linear-2 tiles were measured to spin on the Mixtral shape
-  // (f = 14336: knee 2), so the default lead is max(knee, 8).
+  // rows of a Linear-1 tile, K the participating workgroups and h = f, i.e.
+  // the row bands one sweep of the grid covers (G / N1 here). The knee is a
+  // lower bound that assumes every workgroup advances through Linear-1 at the
+  // same pace. But a workgroup that takes a Linear-2 tile issues no Linear-1
+  // tile for as long as that tile lasts, about f / d Linear-1 tiles of the
+  // same width (the K extents are f and d), so the phase skew between
+  // workgroups, and with it the lead, grows by that factor. Default lead:
+  // max(knee, 8) * max(1, f / d), rounded up. Measured on the Mixtral shape
+  // (f / d = 3.5): D = 8 left Linear-2 tiles waiting 41 us each on average
+  // and the schedule 12% behind D = 32.
   int D = p.lead_D;
   if (D <= 0) {
     D = (G + P.N1 - 1) / P.N1;
     if (D < 8) D = 8;
+    if (p.f > p.d) D = (int)(((int64_t)D * p.f + p.d - 1) / p.d);
   }
   P.lead_D = D;
 

@@ -129,8 +129,9 @@ typedef struct moe_problem {
   int32_t quant_block;   /* fp8 block edge (128); ignored for bf16 */
   int32_t num_segments;  /* S >= 1: destination segments of the output rows */
   int32_t sched;         /* moe_sched_t */
-  int32_t lead_D;        /* interleaved: minimum row lead of Linear-1 over Linear-2 (>= 1);
-                            0 = the anti-starvation knee of X-Stage Eq. 16 */
+  int32_t lead_D;        /* interleaved: minimum row-band lead of Linear-1 over Linear-2 (>= 1);
+                            0 = the anti-starvation knee of X-Stage Eq. 16 (at least 8),
+                            times max(1, f / d), the Linear-2 : Linear-1 tile-time ratio */
   int32_t wave_experts;  /* expert-wave: experts per wave; 0 = fewest experts whose Linear-1
                             tiles fill the persistent grid */
   int32_t grid;          /* persistent workgroups; 0 = one per compute unit */

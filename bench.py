@@ -13,8 +13,11 @@ the average launch duration that the roofline fraction divides by.
 Default workload: the DeepSeek-style share (T=4096 tokens, d=7168, f=2048,
 top-8 of 256 experts, this GPU owns experts 0-31, bf16). Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config NAME] [--sched interleaved|expert_wave|separate]
-                  [--no-cpu-baseline] [--copy-probe]
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--sched auto|interleaved|expert_wave|separate]
+                  [--no-cpu-baseline] [--no-compare] [--trace] [--copy-probe]
+
+After the main measurement the same steps are timed under each explicit
+schedule (schedules_TFLOPs), unless --no-compare.
 """
 from __future__ import annotations
 
@@ -36,10 +39,14 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the GPU reaches its steady clock after a few tens of ms of work")
     ap.add_argument("--config", default="deepseek_share_bf16")
-    ap.add_argument("--sched", default="interleaved", choices=["interleaved", "expert_wave", "separate"])
+    ap.add_argument("--sched", default="auto", choices=["auto", "interleaved", "expert_wave", "separate"],
+                    help="expert-GEMM tile schedule (auto: the library's run-time choice)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the other explicit schedules after the main measurement")
     ap.add_argument("--lead-D", type=int, default=0)
     ap.add_argument("--tiles", default="auto", choices=["auto", "narrow", "wide"],
                     help="expert-GEMM tile width (default: chosen from the shape)")
@@ -167,7 +174,7 @@ def main():
     Y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, p=p):
         if ev is not None:
             ev[0].record(stream)
         moe.route_topk(p, g["logits"], v["topk_idx"], v["topk_w"], None, stream)
@@ -257,7 +264,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) weights, drawn on the GPU)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E_global": cfg.E_global,
                    "k": cfg.k, "local_experts": [cfg.e_begin, cfg.e_end], "segments": cfg.num_segments,
-                   "sched": args.sched, "tiles": args.tiles, "band_major": args.band_major,
+                   "sched": args.sched, "sched_run": moe.schedule_of(p), "tiles": args.tiles,
+                   "band_major": args.band_major,
                    "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "stages_us_median": {n: round(x, 2) for n, x in med.items()},
@@ -266,19 +274,41 @@ def main():
         "combine_GBps": round(comb_bytes / (med["combine"] * 1e-6) / 1e9, 1),
         "roofline": {
             "kernel": "moe_gemm_kernel (grouped Linear-1+SwiGLU+Linear-2, one persistent launch)"
-            if args.sched != "separate" else "moe_gemm_kernel (Linear-1 launch + Linear-2 launch)",
+            if moe.schedule_of(p) != "separate" else "moe_gemm_kernel (Linear-1 launch + Linear-2 launch)",
             "bound": bound,
             "achieved": round(achieved, 1),
             "peak": rpeak,
             "unit": runit,
             "frac": round(achieved / rpeak, 4),
-            "traffic": measured_traffic(cfg, args.sched, args.tiles, args.band_major),
+            "traffic": measured_traffic(cfg, moe.schedule_of(p), args.tiles, args.band_major),
             "algorithmic_bytes_per_launch": gb,
             "useful_flop_per_launch": useful_flop,
             "arithmetic_intensity_flop_per_byte": round(intensity, 1),
             "avg_launch_us": round(gemm_us, 2),
+            "launches_per_call": 2 if moe.schedule_of(p) == "separate" else 1,
+            "avg_launch_us_note": "one moe_expert_forward call: the planning kernel and the GEMM launch(es), "
+                                  "timed back to back with HIP events on the launch stream",
         },
     }
+
+    if not args.no_compare:
+        # the same steps under each explicit schedule (same inputs and workspace)
+        rates = {}
+        for sname in ("separate", "interleaved", "expert_wave"):
+            ps = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end,
+                                  dtype=cfg.dtype, num_segments=cfg.num_segments, sched=sname,
+                                  quant_block=cfg.quant_block, tiles=args.tiles, band_major=args.band_major)
+            for _ in range(args.warmup):
+                step(p=ps)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step(p=ps)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+            moe.check_workspace(ps, ws)
+            rates[sname] = round(useful_flop / dt / 1e12, 2)
+        out["schedules_TFLOPs"] = rates
 
     if args.trace:
         out["tile_trace"] = trace_summary(moe, cfg, args, g, v)

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
     "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
-    "check_workspace", "tile_trace", "SCHED", "DTYPE", "STATUS",
+    "check_workspace", "tile_trace", "schedule_of", "SCHED", "DTYPE", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
           4: "MOE_ERR_HIP", 5: "MOE_ERR_DEADLOCK"}
-SCHED = {"separate": 0, "expert_wave": 1, "interleaved": 2}
+SCHED = {"separate": 0, "expert_wave": 1, "interleaved": 2, "auto": 3}
 DTYPE = {"bf16": 0, "fp8_e4m3": 1}
 # MOE_FLAG_* of moe_mi355x.h
 TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.moe_check_workspace.restype = ctypes.c_int
         L.moe_check_workspace.argtypes = [PP, _P, ctypes.c_size_t, _P]
+        L.moe_schedule_of.restype = ctypes.c_int
+        L.moe_schedule_of.argtypes = [PP]
         L.moe_tile_clock_hz.restype = ctypes.c_double
         L.moe_tile_clock_hz.argtypes = []
         L.moe_status_string.restype = ctypes.c_char_p
@@ -214,6 +216,15 @@ def tile_trace(p: Problem, ws: torch.Tensor) -> Dict[str, "np.ndarray"]:
                 kind=(info & 3).astype(np.int64), nnb=((info >> 2) & 7).astype(np.int64),
                 wg=((info >> 8) & 0xFFFF).astype(np.int64), n=((info >> 24) & 0xFFFF).astype(np.int64),
                 band=(info >> 40).astype(np.int64))
+
+
+def schedule_of(p: Problem) -> str:
+    """The schedule `p` runs, with "auto" resolved."""
+    code = lib().moe_schedule_of(ctypes.byref(p))
+    names = {v: k for k, v in SCHED.items()}
+    if code not in names:
+        raise ValueError(f"schedule_of: invalid schedule {p.sched}")
+    return names[code]
 
 
 def route_topk(p: Problem, logits, topk_idx, topk_w, counts_global=None, stream=None):

@@ -17,7 +17,7 @@ moe_status_t hip_fail(hipError_t e) {
 moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
   if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_INTERLEAVED) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_AUTO) return MOE_ERR_INVALID_ARGUMENT;
   if (p->flags & ~(uint32_t)(MOE_FLAG_TILE_NARROW | MOE_FLAG_TILE_WIDE | MOE_FLAG_BAND_MAJOR | MOE_FLAG_TILE_TRACE))
     return MOE_ERR_INVALID_ARGUMENT;
   if ((p->flags & MOE_FLAG_TILE_NARROW) && (p->flags & MOE_FLAG_TILE_WIDE)) return MOE_ERR_INVALID_ARGUMENT;
@@ -192,6 +192,11 @@ MOE_API const char* moe_status_string(moe_status_t s) {
 MOE_API int moe_last_hip_error(void) { return g_last_hip_error; }
 
 MOE_API const char* moe_version(void) { return "0.1.0"; }
+
+MOE_API int moe_schedule_of(const moe_problem_t* p) {
+  if (!p || p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_AUTO) return -1;
+  return moe::resolve_schedule(*p);
+}
 
 MOE_API double moe_tile_clock_hz(void) {
   int dev = 0, khz = 0;

@@ -186,6 +186,17 @@ TileChoice choose_tiles(const moe_problem_t& p, const Layout&, int) {
   return c;
 }
 
+// MOE_SCHED_AUTO (X-Stage, Section 6.3). The wave and interleaved orders
+// shape remote-store bursts; with the Linear-2 epilogue storing into local
+// HBM there is no drain to shape (every ΔT_iss of X-Stage Eq. 14 is zero), and
+// what they cost stays: a device-scope publish per Linear-1 tile, weight
+// locality shared with the other Linear, and Linear-2 tiles left at the end.
+// Per-tile spans and whole-layer rates on every workload shape put the two
+// separate launches first, so AUTO is SEPARATE.
+int resolve_schedule(const moe_problem_t& p) {
+  return p.sched == MOE_SCHED_AUTO ? MOE_SCHED_SEPARATE : p.sched;
+}
+
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
@@ -193,6 +204,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   const int G = gemm_grid(p);
   if (G <= 0) return hipErrorInvalidDevice;
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const int sched = resolve_schedule(p);
   GemmParams P{};
   P.X = static_cast<const uint8_t*>(X_perm);
   P.W1 = static_cast<const uint8_t*>(W1);
@@ -244,7 +256,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.lead_D = D;
 
   // expert waves need expert-contiguous bands; the other schedules take them largest first
-  const int sort_bands = p.sched == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
+  const int sort_bands = sched == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, sort_bands,
                      L.Pmax,
                      P.blk_done, fp8 ? L.Pmax * (p.f / 128) : 0, reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
@@ -256,11 +268,11 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
     P.mode = mode;
     return fp8 ? launch_gemm_fp8(P, G, s) : launch_gemm_bf16(P, G, s);
   };
-  if (p.sched == MOE_SCHED_SEPARATE) {
+  if (sched == MOE_SCHED_SEPARATE) {
     if ((e = launch(MODE_SEP_L1)) != hipSuccess) return e;
     return launch(MODE_SEP_L2);
   }
-  return launch(p.sched == MOE_SCHED_EXPERT_WAVE ? MODE_WAVE : MODE_INTERLEAVED);
+  return launch(sched == MOE_SCHED_EXPERT_WAVE ? MODE_WAVE : MODE_INTERLEAVED);
 }
 
 }  // namespace moe

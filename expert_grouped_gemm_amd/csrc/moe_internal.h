@@ -121,6 +121,9 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
 
+// The schedule a problem runs (MOE_SCHED_AUTO resolved).
+int resolve_schedule(const moe_problem_t& p);
+
 // Persistent-grid size for the grouped GEMM on the current device.
 int gemm_grid(const moe_problem_t& p);
 

@@ -79,9 +79,15 @@ typedef enum {
                                      Linear-2 tile (stream order is the only dependency) */
   MOE_SCHED_EXPERT_WAVE = 1,      /* one persistent launch; local experts grouped into waves; a wave's
                                      Linear-1 tiles, then its Linear-2 tiles, then the next wave */
-  MOE_SCHED_INTERLEAVED = 2       /* one persistent launch; Linear-1 and Linear-2 tile streams merged:
+  MOE_SCHED_INTERLEAVED = 2,      /* one persistent launch; Linear-1 and Linear-2 tile streams merged:
                                      a Linear-2 tile of row p2 is taken only when the Linear-1 cursor
                                      leads by at least lead_D rows, otherwise a Linear-1 tile */
+  MOE_SCHED_AUTO = 3              /* chosen at run time (X-Stage, Section 6.3: pick the schedule per
+                                     routing and working set). The expert-wave and interleaved orders
+                                     exist to spread remote-store bursts; this library's epilogues
+                                     store into local HBM, where nothing drains them, so the choice is
+                                     MOE_SCHED_SEPARATE, which needs no cross-workgroup readiness
+                                     counters (measured fastest on every workload shape here) */
 } moe_sched_t;
 
 /* Tile-shape controls of the grouped expert GEMMs. Every combination gives
@@ -225,6 +231,9 @@ MOE_API const char* moe_status_string(moe_status_t s);
 MOE_API int moe_last_hip_error(void);
 /* Library version, e.g. "0.1.0". */
 MOE_API const char* moe_version(void);
+/* The schedule `p` runs: p->sched, with MOE_SCHED_AUTO resolved; -1 if
+ * p->sched is not a moe_sched_t. */
+MOE_API int moe_schedule_of(const moe_problem_t* p);
 /* Frequency in Hz of the clock the moe_tile_record_t readings count (the
  * current device's constant-rate wall clock), or 0 if HIP cannot report it. */
 MOE_API double moe_tile_clock_hz(void);

@@ -66,7 +66,7 @@ def test_unsupported_shapes(L, over, code):
 
 
 def test_invalid_enums_and_flags(L):
-    for field, val in (("dtype", 7), ("sched", 3), ("flags", 3), ("flags", 16), ("lead_D", -1), ("grid", -2)):
+    for field, val in (("dtype", 7), ("sched", 4), ("flags", 3), ("flags", 16), ("lead_D", -1), ("grid", -2)):
         p = moe.make_problem(**GOOD)
         setattr(p, field, val)
         out = moe.WorkspaceLayout()
@@ -115,3 +115,14 @@ def test_binding_rejects_cpu_tensors():
     p = moe.make_problem(**GOOD)
     with pytest.raises(ValueError):
         moe.route_topk(p, torch.zeros(64, 4), torch.zeros(64, 2, dtype=torch.int32), torch.zeros(64, 2))
+
+
+def test_schedule_of_resolves_auto(L):
+    for name, code in moe.SCHED.items():
+        p = moe.make_problem(**GOOD, sched=name)
+        assert L.moe_schedule_of(ctypes.byref(p)) == (moe.SCHED["separate"] if name == "auto" else code)
+    assert moe.schedule_of(moe.make_problem(**GOOD, sched="auto")) == "separate"
+    p = moe.make_problem(**GOOD)
+    p.sched = 4
+    assert L.moe_schedule_of(ctypes.byref(p)) == -1
+    assert L.moe_schedule_of(None) == -1

@@ -37,7 +37,7 @@ def _covered(spans, total):
 
 @pytest.mark.parametrize("kw", [dict(sched="separate"), dict(sched="separate", grid=6),
                                 dict(sched="expert_wave"), dict(sched="interleaved"),
-                                dict(sched="interleaved", tiles="narrow")], ids=str)
+                                dict(sched="interleaved", tiles="narrow"), dict(sched="auto")], ids=str)
 @pytest.mark.parametrize("name", list(CFGS))
 def test_tile_trace(name, kw):
     import expert_grouped_gemm_amd as moe
@@ -73,7 +73,7 @@ def test_tile_trace(name, kw):
         sel = np.flatnonzero(tr["wg"] == w)
         order = sel[np.argsort(ts[sel], kind="stable")]
         assert np.all(ts[order[1:]] >= te[order[:-1]]), w
-    if kw["sched"] == "separate":
+    if moe.schedule_of(p) == "separate":  # two launches (auto resolves to them)
         assert ts[kind == 2].min() >= te[kind == 1].max()
     else:
         for b in range(nb):

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
     "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
-    "check_workspace", "tile_trace", "schedule_of", "SCHED", "DTYPE", "STATUS",
+    "check_workspace", "tile_trace", "schedule_of", "store_burst_probe", "SCHED", "DTYPE", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.moe_check_workspace.restype = ctypes.c_int
         L.moe_check_workspace.argtypes = [PP, _P, ctypes.c_size_t, _P]
+        L.moe_store_burst_probe.restype = ctypes.c_int
+        L.moe_store_burst_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _P,
+                                            ctypes.c_size_t, _P, ctypes.c_size_t, _P]
         L.moe_schedule_of.restype = ctypes.c_int
         L.moe_schedule_of.argtypes = [PP]
         L.moe_tile_clock_hz.restype = ctypes.c_double
@@ -216,6 +219,16 @@ def tile_trace(p: Problem, ws: torch.Tensor) -> Dict[str, "np.ndarray"]:
                 kind=(info & 3).astype(np.int64), nnb=((info >> 2) & 7).astype(np.int64),
                 wg=((info >> 8) & 0xFFFF).astype(np.int64), n=((info >> 24) & 0xFFFF).astype(np.int64),
                 band=(info >> 40).astype(np.int64))
+
+
+def store_burst_probe(K: int, B: int, reps: int, gap_us: float, buf: torch.Tensor, rec: torch.Tensor,
+                      stream=None):
+    """moe_store_burst_probe: K producers, reps bursts of B bytes with gap_us
+    between them, into `buf` (device bytes); clock readings into `rec`
+    (device int64, at least 2*K*reps + 1 elements)."""
+    _check(lib().moe_store_burst_probe(K, B, reps, gap_us, _ptr(buf), buf.numel() * buf.element_size(), _ptr(rec),
+                                       rec.numel() * rec.element_size(), _stream(stream)),
+           "moe_store_burst_probe")
 
 
 def schedule_of(p: Problem) -> str:

@@ -177,6 +177,19 @@ MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace
   return MOE_OK;
 }
 
+MOE_API moe_status_t moe_store_burst_probe(int K, int B, int reps, double gap_us, void* buf, size_t buf_bytes,
+                                           uint64_t* rec, size_t rec_bytes, void* stream) {
+  if (K < 1 || K > 4096 || B < 1024 || (B % 1024) != 0 || reps < 1 || reps > 100000) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(gap_us >= 0.0 && gap_us <= 1e5)) return MOE_ERR_INVALID_ARGUMENT;  // also rejects NaN
+  if (gap_us * reps > 2e6) return MOE_ERR_INVALID_ARGUMENT;                // at most 2 s of gaps per launch
+  if (!buf || !rec) return MOE_ERR_INVALID_ARGUMENT;
+  if (((buf_bytes / (size_t)K) & ~(size_t)1023) < (size_t)B) return MOE_ERR_INVALID_ARGUMENT;
+  if (rec_bytes < ((size_t)2 * K * reps + 1) * sizeof(uint64_t)) return MOE_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(rec) % 8) return MOE_ERR_INVALID_ARGUMENT;
+  const hipError_t e = moe::launch_store_burst(K, B, reps, gap_us, buf, buf_bytes, rec, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 MOE_API const char* moe_status_string(moe_status_t s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -121,6 +121,10 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
 
+// Store-burst probe (validated arguments; see moe_store_burst_probe).
+hipError_t launch_store_burst(int K, int B, int reps, double gap_us, void* buf, size_t buf_bytes, uint64_t* rec,
+                              hipStream_t s);
+
 // The schedule a problem runs (MOE_SCHED_AUTO resolved).
 int resolve_schedule(const moe_problem_t& p);
 

@@ -231,6 +231,24 @@ MOE_API const char* moe_status_string(moe_status_t s);
 MOE_API int moe_last_hip_error(void);
 /* Library version, e.g. "0.1.0". */
 MOE_API const char* moe_version(void);
+/* Store-burst probe: the local-memory form of the periodic and isolated
+ * burst microbenchmarks of X-Stage, Section 3.1, whose timings calibrate the
+ * Burst-Gap parameters (T_iss^0, R, Q; Section 3.2-3.5, Eqs. 1-7) for vector
+ * stores the CUs issue into their own HBM.
+ *   K producers (1..4096; one wavefront each) start together and repeat
+ *   `reps` times (1..100000): a burst of B bytes (a multiple of 1024, at
+ *   least 1024) of 16-byte stores, then a gap of gap_us microseconds
+ *   (0..100000, and reps * gap_us at most 2 s) with no memory traffic. Producer k writes its own ring of
+ *   buf_bytes / K bytes (rounded down to 1 KiB; at least B) of `buf`
+ *   (device memory, contents overwritten).
+ *   rec: device memory of at least (2 K reps + 1) 64-bit words; word
+ *   2 (k reps + r) is producer k's clock reading at the start of burst r,
+ *   the next word the reading once its last store has issued; the last word
+ *   is the common start time. Clock rate: moe_tile_clock_hz().
+ *   Invalid arguments return MOE_ERR_INVALID_ARGUMENT before any launch. */
+MOE_API moe_status_t moe_store_burst_probe(int K, int B, int reps, double gap_us, void* buf, size_t buf_bytes,
+                                           uint64_t* rec, size_t rec_bytes, void* stream);
+
 /* The schedule `p` runs: p->sched, with MOE_SCHED_AUTO resolved; -1 if
  * p->sched is not a moe_sched_t. */
 MOE_API int moe_schedule_of(const moe_problem_t* p);

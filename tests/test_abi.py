@@ -126,3 +126,20 @@ def test_schedule_of_resolves_auto(L):
     p.sched = 4
     assert L.moe_schedule_of(ctypes.byref(p)) == -1
     assert L.moe_schedule_of(None) == -1
+
+
+def test_store_burst_probe_rejects_bad_arguments(L):
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails first
+    ok = dict(K=4, B=4096, reps=3, gap=1.0, buf_bytes=4 * 8192, rec_bytes=(2 * 4 * 3 + 1) * 8)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return L.moe_store_burst_probe(a["K"], a["B"], a["reps"], ctypes.c_double(a["gap"]), fake,
+                                       ctypes.c_size_t(a["buf_bytes"]), fake, ctypes.c_size_t(a["rec_bytes"]),
+                                       None)
+    for over in (dict(K=0), dict(K=5000), dict(B=1000), dict(B=0), dict(reps=0), dict(gap=-1.0),
+                 dict(gap=float("nan")), dict(gap=2e5), dict(gap=1e5, reps=21), dict(buf_bytes=4 * 4096 - 1), dict(rec_bytes=24 * 8)):
+        assert call(**over) == 1, over
+    assert L.moe_store_burst_probe(4, 4096, 3, ctypes.c_double(1.0), None, ctypes.c_size_t(1 << 20), fake,
+                                   ctypes.c_size_t(1 << 20), None) == 1

@@ -33,6 +33,7 @@ DTYPE = {"bf16": 0, "fp8_e4m3": 1}
 TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
 FLAG_BAND_MAJOR = 4
 FLAG_TILE_TRACE = 8
+FLAG_KEEP_H_F32 = 16
 
 
 class MoEError(RuntimeError):
@@ -108,11 +109,13 @@ def lib() -> ctypes.CDLL:
 def make_problem(T: int, d: int, f: int, E_global: int, k: int, e_begin: int = 0, e_end: Optional[int] = None,
                  dtype: str = "bf16", num_segments: int = 1, sched: str = "interleaved", lead_D: int = 0,
                  wave_experts: int = 0, grid: int = 0, quant_block: int = 128, tiles: str = "auto",
-                 band_major: bool = False, trace: bool = False) -> Problem:
+                 band_major: bool = False, trace: bool = False, keep_h_f32: bool = False) -> Problem:
     """tiles: "auto" (chosen from the shape), "narrow" or "wide" expert-GEMM tiles;
     band_major: walk the separate / expert-wave tile lists band by band;
-    trace: record one timed span per expert-GEMM tile (read with tile_trace)."""
-    flags = TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0) | (FLAG_TILE_TRACE if trace else 0)
+    trace: record one timed span per expert-GEMM tile (read with tile_trace);
+    keep_h_f32: fp8, store every fp32 SwiGLU value in the workspace view h_f32."""
+    flags = (TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0) | (FLAG_TILE_TRACE if trace else 0)
+             | (FLAG_KEEP_H_F32 if keep_h_f32 else 0))
     return Problem(T=T, d=d, f=f, E_global=E_global, k=k, e_begin=e_begin,
                    e_end=E_global if e_end is None else e_end, dtype=DTYPE[dtype], quant_block=quant_block,
                    num_segments=num_segments, sched=SCHED[sched], lead_D=lead_D, wave_experts=wave_experts,

@@ -236,6 +236,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.blk_done = reinterpret_cast<int32_t*>(ws + L.blk_done);
   P.trace = L.pub.tile_trace_capacity ? reinterpret_cast<uint64_t*>(ws + L.pub.tile_trace) : nullptr;
   P.trace_cap = (int)L.pub.tile_trace_capacity;
+  P.keep_hf = (p.flags & MOE_FLAG_KEEP_H_F32) ? 1 : 0;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile, K the participating workgroups and h = f, i.e.
   // the row bands one sweep of the grid covers (G / N1 here). The knee is a

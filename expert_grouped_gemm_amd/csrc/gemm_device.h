@@ -94,6 +94,7 @@ struct GemmParams {
   int ready;              // l2_full value at which a row band's H is complete (N1, or f/128 with fp8)
   uint64_t* trace;        // tile records of 5 words (moe_tile_record_t), or null: no timing
   int trace_cap;          // records the trace region holds
+  int keep_hf;            // fp8: wide Linear-1 tiles also store their fp32 SwiGLU values in Hf
 };
 
 // Launch the persistent expert-GEMM kernel of one operand type (bf16 in
@@ -389,9 +390,15 @@ __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int 
 
 // Accumulator element i of a 32x32 block sits at row 8*(i/4) + 4*(lane/32) + i%4,
 // column lane%32.
+// fp8 Linear-1 tiles of the wide width own a whole 128-column quantisation
+// block: they stage its fp32 SwiGLU values in the (free) LDS ring as
+// [rows][128] floats and quantise from there (quantize_block_lds).
+template <int NNB, bool L1, bool FP8>
+constexpr bool stages_block_in_lds() { return FP8 && L1 && NNB * 32 == 128; }
+
 template <int NMB, int NNB, bool L1, bool FP8>
 __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
-                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
+                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB], lds_t* lds) {
   using G = WaveGrid<NNB, FP8>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
@@ -408,10 +415,17 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
           for (int c = 0; c < G::CPH; ++c) {
             const float g = acc[mi][c][i], u = acc[mi][G::CPH + c][i];
             const float act = g / (1.0f + expf(-g)) * u;
-            const int col = t.n * (NNB * 32) + wave_col<NNB, FP8>(0, c, wn, lr);
+            const int cb = wave_col<NNB, FP8>(0, c, wn, lr);
+            const int col = t.n * (NNB * 32) + cb;
             const size_t at = (size_t)(t.row0 + m) * P.f + col;
-            if constexpr (FP8) P.Hf[at] = act;  // quantised per 128-column block once it is stored
-            else reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
+            if constexpr (stages_block_in_lds<NNB, L1, FP8>()) {
+              reinterpret_cast<__attribute__((address_space(3))) float*>(lds)[m * 128 + cb] = act;
+              if (P.keep_hf) P.Hf[at] = act;
+            } else if constexpr (FP8) {
+              P.Hf[at] = act;  // quantised per 128-column block once both halves are stored
+            } else {
+              reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
+            }
           }
         } else {
           const int dst = P.row_dst[t.row0 + m];
@@ -491,7 +505,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
   }
   lds_barrier();  // LDS ring free for the next tile
   if (P.trace) t_main = __builtin_amdgcn_s_memrealtime();
-  if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc);
+  if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc, lds);
 }
 
 // MB = the band's 32-row blocks. With two wavefront rows (WM = 2) wavefront
@@ -581,7 +595,11 @@ __device__ __forceinline__ int publish(int32_t* counter, int inc) {
 // scale), round to nearest even. 16 lanes per row (8 values each), one row
 // per 16 threads per pass; the loads of four passes are issued before any is
 // used.
-__device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
+// The values come from Hf (in HBM) or, for a block a wide tile staged, from
+// the LDS ring ([rows][128] floats); the arithmetic is the same.
+template <bool FROM_LDS>
+__device__ __forceinline__ void quantize_block_from(const GemmParams& P, int row0, int rows, int j,
+                                                    const lds_t* lds) {
   constexpr int RPP = gemm_threads(true) / 16;  // rows per pass
   const int rr = threadIdx.x >> 4, q = threadIdx.x & 15;
   const int col = j * 128 + q * 8;
@@ -591,9 +609,16 @@ __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
     for (int u = 0; u < 4; ++u) {
       const int r = base + u * RPP + rr;
       if (r < rows) {
-        const float4* src = reinterpret_cast<const float4*>(P.Hf + (size_t)(row0 + r) * P.f + col);
-        v[u][0] = src[0];
-        v[u][1] = src[1];
+        if constexpr (FROM_LDS) {
+          typedef __attribute__((address_space(3))) const float lds_f;
+          lds_f* src = reinterpret_cast<lds_f*>(lds) + r * 128 + q * 8;
+          v[u][0] = make_float4(src[0], src[1], src[2], src[3]);
+          v[u][1] = make_float4(src[4], src[5], src[6], src[7]);
+        } else {
+          const float4* src = reinterpret_cast<const float4*>(P.Hf + (size_t)(row0 + r) * P.f + col);
+          v[u][0] = src[0];
+          v[u][1] = src[1];
+        }
       }
     }
 #pragma unroll
@@ -616,12 +641,15 @@ __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
   }
 }
 
+__device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
+  quantize_block_from<false>(P, row0, rows, j, nullptr);
+}
+
 // After a Linear-1 tile's stores. bf16 (fused schedules only): count the tile
 // in l2_full[p]; the band is ready at N1. fp8: the 128-column block j is
-// covered by 128 / (32 nnb1) tiles (2 narrow, 1 wide). A wide tile quantises
-// its own block as soon as its workgroup's Hf stores are done (each wave
-// waits for its stores, then the barrier: no other CU wrote or read those
-// lines, so nothing needs a device-scope release or a cache write-back). Narrow tiles each count themselves in blk_done[p][j] at
+// covered by 128 / (32 nnb1) tiles (2 narrow, 1 wide). A wide tile staged
+// its block in the LDS ring (the epilogue) and quantises it from there, with
+// no round trip through HBM and no device-scope counter. Narrow tiles each count themselves in blk_done[p][j] at
 // device scope, and the second (every Hf store of the block is then
 // published) quantises it. In the fused schedules the quantised block is
 // counted in l2_full[p]; the band is ready at f / 128. The separate schedule
@@ -635,9 +663,9 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
     const int j = (t.n * bn1) >> 7;
     const int need = 128 / bn1;
     if (need == 1) {
-      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's Hf stores are done
-      __syncthreads();
-      quantize_block(P, t.row0, t.rows, j);
+      __syncthreads();  // every wave's values are in the LDS block
+      quantize_block_from<true>(P, t.row0, t.rows, j, lds);
+      __syncthreads();  // the ring is reused by the next tile
       if (fused) publish(P.l2_full + p, 1);
       return;
     }

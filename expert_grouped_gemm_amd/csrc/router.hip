@@ -50,6 +50,7 @@ __device__ __forceinline__ int wave_min_i32(int x) {
              min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
+template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
@@ -59,14 +60,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (t >= T) return;  // whole wavefronts: the DPP reductions need every lane
   const float* row = logits + (size_t)t * E;
 
-  constexpr int kMaxPer = 16;
-  float v[kMaxPer];
-  const int per = (E + 63) >> 6;
+  // PER = ceil(E / 64) logits per lane (1, 2, 4, 8 or 16): the selection
+  // scans only the slots that exist
+  float v[PER];
   uint32_t taken = 0;  // bit i: slot i of this lane already selected (or absent)
 #pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    const bool present = i < per && e < E;
+    const bool present = e < E;
     v[i] = present ? row[e] : 0.0f;
     if (!present) taken |= 1u << i;
   }
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     float best = -__builtin_huge_valf();
     int best_i = -1;
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i)
+    for (int i = 0; i < PER; ++i)
       if (!(taken & (1u << i)) && (best_i < 0 || v[i] > best)) {
         best = v[i];
         best_i = i;
@@ -118,8 +119,16 @@ hipError_t launch_route(const moe_problem_t& p, const float* logits, int32_t* id
     if (e != hipSuccess) return e;
   }
   const int blocks = (p.T + kRouteWaves - 1) / kRouteWaves;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(64 * kRouteWaves), 0, s, logits, p.T, p.E_global,
-                     p.k, idx, w, counts_global);
+  const int per = (p.E_global + 63) >> 6;  // E_global <= 1024 (validated)
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kRouteWaves), 0, s, logits, p.T, p.E_global, p.k, idx, w,
+                       counts_global);
+  };
+  if (per <= 1) go(route_topk_kernel<1>);
+  else if (per <= 2) go(route_topk_kernel<2>);
+  else if (per <= 4) go(route_topk_kernel<4>);
+  else if (per <= 8) go(route_topk_kernel<8>);
+  else go(route_topk_kernel<16>);
   return hipGetLastError();
 }
 

@@ -101,8 +101,12 @@ enum {
                                      d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
   MOE_FLAG_BAND_MAJOR = 4u,       /* walk the expert-GEMM tile lists row band by row band instead of
                                      in groups of bands */
-  MOE_FLAG_TILE_TRACE = 8u        /* record one span per expert-GEMM tile in the workspace region
+  MOE_FLAG_TILE_TRACE = 8u,       /* record one span per expert-GEMM tile in the workspace region
                                      tile_trace (moe_tile_record_t); costs a few clock reads per tile */
+  MOE_FLAG_KEEP_H_F32 = 16u       /* fp8: also store every fp32 SwiGLU value (the H quantiser's input)
+                                     in the workspace region h_f32. Without it, wide Linear-1 tiles
+                                     quantise from on-chip memory and leave h_f32 unwritten. For
+                                     verification; costs 4 bytes of HBM writes per H element */
 };
 
 /* One expert-GEMM tile as recorded with MOE_FLAG_TILE_TRACE: the per-tile

@@ -59,7 +59,7 @@ def test_fp8_h_quantiser_bit_exact(name, tiles):
     quantises it), wide tiles a whole block."""
     import expert_grouped_gemm_amd as moe
     cfg = FP8[name]
-    inp, g, p, Y, Y32, ws = _run(cfg, tiles=tiles)
+    inp, g, p, Y, Y32, ws = _run(cfg, tiles=tiles, keep_h_f32=True)
     v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items()}
     A = int(v["meta"][0])
     hf = v["h_f32"].numpy()[:A].astype(np.float32)
@@ -89,6 +89,7 @@ def test_fp8_schedule_invariance_bitwise():
     g = to_gpu(moe_synth.generate(cfg))
     base, _, _ = run_layer(problem_of(cfg, sched="separate"), g, want_fp32=False)
     for kw in (dict(sched="expert_wave"), dict(sched="interleaved"), dict(sched="interleaved", lead_D=1, grid=8),
+               dict(sched="separate", keep_h_f32=True), dict(sched="separate", tiles="narrow"),
                dict(sched="separate", tiles="wide"), dict(sched="interleaved", tiles="wide"),
                dict(sched="separate", tiles="narrow", band_major=True)):
         Y, _, _ = run_layer(problem_of(cfg, **kw), g, want_fp32=False)

@@ -47,7 +47,10 @@
 //                     the Linear-1 cursor's group leads p2 by at least D bands
 //                     (with group_m = 1: the Linear-1 cursor's band, as in the
 //                     algorithm), otherwise the next Linear-1 tile; the N-tile
-//                     of pair column c is n = 2 c + r.
+//                     of pair column c is n = 2 c + r. With wide Linear-2
+//                     tiles, the pair columns of a last, partly idle round
+//                     run after a workgroup's Linear-1 tiles as narrow
+//                     tiles dealt over all workgroups.
 // l2_full[p] counts stored Linear-1 tiles of row p (X-Stage Section 4.2,
 // "Condition 2"): the Linear-1 epilogue publishes with an agent-scope release
 // after its H stores, a Linear-2 tile of row p acquires once it reaches the
@@ -56,7 +59,7 @@
 // tiles all precede its cursor; so the workgroup holding the earliest
 // unfinished Linear-1 tile either runs it or waits on a band that is already
 // complete (no deadlock while the whole grid is resident: one workgroup per
-// CU). Waits are bounded; a
+// CU). A workgroup in the narrow tail holds no Linear-1 tile. Waits are bounded; a
 // timeout sets the sticky error flag meta[META_ERR].
 #pragma once
 
@@ -833,14 +836,18 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
       const int P1 = (P.N1 + 1) >> 1, P2 = (P.N2 + 1) >> 1;
       const int end1 = Pb * P1, end2 = Pb * P2;
       const int span1 = P.group_m * P1;
+      // With wide Linear-2 tiles, a last round that would leave pairs idle
+      // (end2 not a multiple of Gp) runs after this loop as narrow tiles
+      // spread over every workgroup, as in the separate schedule.
+      const int cut2 = (P.nnb2 == 4 && end2 % Gp) ? end2 / Gp * Gp : end2;
       int k1 = g, k2 = g;
-      while (k1 < end1 || k2 < end2) {
+      while (k1 < end1 || k2 < cut2) {
         // first band of k1's raster group: every Linear-1 tile of a lower band
         // comes before k1 in the Linear-1 order
         const int b1 = k1 < end1 ? (k1 / span1) * P.group_m : 0x3FFFFFFF;
         int p2 = 0, c2 = 0;
-        if (k2 < end2) raster(k2, Pb, P2, P.group_m, p2, c2);
-        if (k2 < end2 && p2 + P.lead_D <= b1) {
+        if (k2 < cut2) raster(k2, Pb, P2, P.group_m, p2, c2);
+        if (k2 < cut2 && p2 + P.lead_D <= b1) {
           const int n = 2 * c2 + r;
           if (n < P.N2) do_tile<false, FP8>(P, p2, n, P.nnb2, true, lds);
           k2 += Gp;
@@ -851,6 +858,16 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
           if (n < P.N1) do_tile<true, FP8>(P, p1, n, P.nnb1, true, lds);
           k1 += Gp;
         }
+      }
+      // The tail: pair unit cut2 + (j >> 2) holds wide tiles 2 c2 and 2 c2 + 1,
+      // i.e. narrow tiles 4 c2 .. 4 c2 + 3 (those of a wide tile past N2 do not
+      // exist). A workgroup gets here only after its own Linear-1 tiles, so
+      // every readiness wait below is on tiles that workgroups still in the
+      // loop above issue.
+      for (int j = lid; j < 4 * (end2 - cut2); j += G) {
+        int p2, c2;
+        raster(cut2 + (j >> 2), Pb, P2, P.group_m, p2, c2);
+        if (2 * c2 + ((j >> 1) & 1) < P.N2) do_tile<false, FP8>(P, p2, 4 * c2 + (j & 3), 2, true, lds);
       }
       break;
     }

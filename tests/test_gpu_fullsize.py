@@ -1,5 +1,6 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (interleaved schedule, default lead and grid).
+benchmark times (the run-time schedule choice, default tiles and grid) and in
+the interleaved schedule.
 
 Routing, counts, offsets and the whole dispatch permutation are compared
 bit-exactly with the oracle; Y is compared on sampled output rows the oracle
@@ -19,12 +20,13 @@ pytestmark = pytest.mark.gpu
 FULL = ["deepseek_share_bf16", "dit_skewed", "mixtral", "deepseek_share_fp8"]
 
 
+@pytest.mark.parametrize("sched", ["auto", "interleaved"])
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_parity(name):
+def test_full_size_parity(name, sched):
     import expert_grouped_gemm_amd as moe
     cfg = moe_synth.CONFIGS[name]
     g = moe_synth.generate(cfg, device="cuda")
-    p = problem_of(cfg)
+    p = problem_of(cfg, sched=sched)
     Y, Y32, ws = run_layer(p, g)
     moe.check_workspace(p, ws)
     v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items() if k not in ("x_perm", "h", "h_f32", "combine_buf")}
@@ -55,7 +57,7 @@ def test_full_size_parity(name):
         qz = oracle.y_row_of_token(without, cfg.T, cfg.num_segments)
         assert np.all(Y.float().cpu().numpy()[qz] == 0.0)
     check_y(Yh, ref["Y"][q], None if cfg.dtype == "fp8_e4m3" else Y32.cpu().numpy()[q],
-            fp8=cfg.dtype == "fp8_e4m3", label=name)
+            fp8=cfg.dtype == "fp8_e4m3", label=f"{name}/{sched}")
     # x_perm rows of the sampled tokens were gathered exactly
     xp = moe.workspace_views(p, ws)["x_perm"]
     rows = np.flatnonzero(np.isin(disp["row_src"] // cfg.k, with_local))[:32]

@@ -1,0 +1,60 @@
+"""Degenerate shares against the oracle, in every schedule and both tile
+widths:
+
+* no local assignment at all (the local experts are never in any token's
+  top-k): A = 0, no row band reaches the expert GEMMs, and Y is exactly zero;
+* a single token routed to a single expert (T = 1, k = 1, E = 1);
+* one token per destination segment with a local share that gets only some
+  of them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from moe_cases import check_y, problem_of, run_layer, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = ["separate", "expert_wave", "interleaved", "auto"]
+
+
+def _cases():
+    # local experts 6 and 7 are pushed out of every top-2
+    no_local = moe_synth.make_config("tiny", T=300, d=128, f=256, E_global=8, k=2, e_begin=6, e_end=8, seed=31)
+    inp = moe_synth.generate(no_local)
+    inp["logits"][:, 6:8] = -1.0e4
+    yield "no_local", no_local, inp
+    single = moe_synth.make_config("tiny", T=1, d=128, f=128, E_global=1, k=1, e_begin=0, e_end=1, seed=32)
+    yield "single_token", single, moe_synth.generate(single)
+    seg = moe_synth.make_config("tiny", T=8, d=256, f=128, E_global=4, k=2, e_begin=1, e_end=3, num_segments=8,
+                                seed=33)
+    yield "token_per_segment", seg, moe_synth.generate(seg)
+
+
+CASES = {name: (cfg, inp) for name, cfg, inp in _cases()}
+
+
+@pytest.mark.parametrize("tiles", ["narrow", "wide"])
+@pytest.mark.parametrize("sched", SCHEDS)
+@pytest.mark.parametrize("name", list(CASES))
+def test_degenerate_share(name, sched, tiles):
+    import expert_grouped_gemm_amd as moe
+    cfg, inp = CASES[name]
+    ref = oracle.moe_layer(inp, cfg)
+    p = problem_of(cfg, sched=sched, tiles=tiles)
+    Y, Y32, ws = run_layer(p, to_gpu(inp))
+    moe.check_workspace(p, ws)
+    v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items()}
+    A = ref["A"]
+    assert int(v["meta"][0]) == A
+    np.testing.assert_array_equal(v["topk_idx"].numpy(), ref["topk_idx"])
+    np.testing.assert_array_equal(v["tok_off"].numpy(), ref["tok_off"])
+    np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
+    if name == "no_local":
+        assert A == 0 and int(v["meta"][1]) == 0
+        assert torch.count_nonzero(Y.float()).item() == 0 and torch.count_nonzero(Y32).item() == 0
+    else:
+        assert A > 0
+        check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=f"{name}/{sched}/{tiles}")

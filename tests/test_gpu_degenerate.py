@@ -58,3 +58,35 @@ def test_degenerate_share(name, sched, tiles):
     else:
         assert A > 0
         check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=f"{name}/{sched}/{tiles}")
+
+
+# Router widths: ceil(E / 64) logits per lane = 2, 8 and 16 (E = 1024 and
+# k = 16 are the largest the library accepts); the whole layer on a local
+# share, with routing and dispatch compared bit for bit.
+WIDE_E = {
+    "E100_k8": moe_synth.make_config("tiny", T=256, d=128, f=128, E_global=100, k=8, e_begin=10, e_end=60, seed=41),
+    "E300_k16": moe_synth.make_config("tiny", T=192, d=128, f=128, E_global=300, k=16, e_begin=0, e_end=300,
+                                      seed=42),
+    "E1024_k16": moe_synth.make_config("tiny", T=128, d=128, f=128, E_global=1024, k=16, e_begin=512, e_end=1024,
+                                       num_segments=2, seed=43),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_E))
+def test_router_widths_and_large_expert_counts(name):
+    import expert_grouped_gemm_amd as moe
+    cfg = WIDE_E[name]
+    inp = moe_synth.generate(cfg)
+    ref = oracle.moe_layer(inp, cfg)
+    p = problem_of(cfg, sched="auto")
+    Y, Y32, ws = run_layer(p, to_gpu(inp))
+    moe.check_workspace(p, ws)
+    v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items()}
+    A = ref["A"]
+    np.testing.assert_array_equal(v["topk_idx"].numpy(), ref["topk_idx"])
+    np.testing.assert_allclose(v["topk_w"].numpy(), ref["topk_w"], rtol=2e-6, atol=1e-7)
+    for key in ("counts", "offsets", "tok_off"):
+        np.testing.assert_array_equal(v[key].numpy(), ref[key], err_msg=key)
+    np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
+    np.testing.assert_array_equal(v["row_dst"].numpy()[:A], ref["row_dst"])
+    check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=name)

@@ -34,6 +34,7 @@ TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
 FLAG_BAND_MAJOR = 4
 FLAG_TILE_TRACE = 8
 FLAG_KEEP_H_F32 = 16
+FLAG_TEST_WAIT_TIMEOUT = 32
 
 
 class MoEError(RuntimeError):

@@ -19,7 +19,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
   if (p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_AUTO) return MOE_ERR_INVALID_ARGUMENT;
   if (p->flags & ~(uint32_t)(MOE_FLAG_TILE_NARROW | MOE_FLAG_TILE_WIDE | MOE_FLAG_BAND_MAJOR | MOE_FLAG_TILE_TRACE |
-                                MOE_FLAG_KEEP_H_F32))
+                                MOE_FLAG_KEEP_H_F32 | MOE_FLAG_TEST_WAIT_TIMEOUT))
     return MOE_ERR_INVALID_ARGUMENT;
   if ((p->flags & MOE_FLAG_TILE_NARROW) && (p->flags & MOE_FLAG_TILE_WIDE)) return MOE_ERR_INVALID_ARGUMENT;
   if (p->lead_D < 0 || p->wave_experts < 0 || p->grid < 0) return MOE_ERR_INVALID_ARGUMENT;

@@ -233,6 +233,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.N1 = p.f / (32 * tc.nnb1);
   P.N2 = p.d / (64 * tc.nnb2);
   P.ready = fp8 ? p.f / 128 : P.N1;
+  if (p.flags & MOE_FLAG_TEST_WAIT_TIMEOUT) P.ready = 0x7FFFFFFF;  // no band ever becomes ready
   P.blk_done = reinterpret_cast<int32_t*>(ws + L.blk_done);
   P.trace = L.pub.tile_trace_capacity ? reinterpret_cast<uint64_t*>(ws + L.pub.tile_trace) : nullptr;
   P.trace_cap = (int)L.pub.tile_trace_capacity;

@@ -103,10 +103,15 @@ enum {
                                      in groups of bands */
   MOE_FLAG_TILE_TRACE = 8u,       /* record one span per expert-GEMM tile in the workspace region
                                      tile_trace (moe_tile_record_t); costs a few clock reads per tile */
-  MOE_FLAG_KEEP_H_F32 = 16u       /* fp8: also store every fp32 SwiGLU value (the H quantiser's input)
+  MOE_FLAG_KEEP_H_F32 = 16u,      /* fp8: also store every fp32 SwiGLU value (the H quantiser's input)
                                      in the workspace region h_f32. Without it, wide Linear-1 tiles
                                      quantise from on-chip memory and leave h_f32 unwritten. For
                                      verification; costs 4 bytes of HBM writes per H element */
+  MOE_FLAG_TEST_WAIT_TIMEOUT = 32u /* tests of the timeout path only: the fused schedules' readiness
+                                     target is made unreachable, so their first Linear-2 wait gives up
+                                     after its bounded spin (about a second), every later wait at once,
+                                     and moe_check_workspace reports MOE_ERR_DEADLOCK. Outputs are
+                                     then invalid. The separate schedule has no such wait */
 };
 
 /* One expert-GEMM tile as recorded with MOE_FLAG_TILE_TRACE: the per-tile

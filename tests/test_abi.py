@@ -66,7 +66,7 @@ def test_unsupported_shapes(L, over, code):
 
 
 def test_invalid_enums_and_flags(L):
-    for field, val in (("dtype", 7), ("sched", 4), ("flags", 3), ("flags", 32), ("lead_D", -1), ("grid", -2)):
+    for field, val in (("dtype", 7), ("sched", 4), ("flags", 3), ("flags", 64), ("lead_D", -1), ("grid", -2)):
         p = moe.make_problem(**GOOD)
         setattr(p, field, val)
         out = moe.WorkspaceLayout()

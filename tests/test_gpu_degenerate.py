@@ -2,7 +2,8 @@
 widths:
 
 * no local assignment at all (the local experts are never in any token's
-  top-k): A = 0, no row band reaches the expert GEMMs, and Y is exactly zero;
+  top-k), bf16 and fp8: A = 0, no row band reaches the expert GEMMs, and Y
+  is exactly zero;
 * a single token routed to a single expert (T = 1, k = 1, E = 1);
 * one token per destination segment with a local share that gets only some
   of them.
@@ -26,6 +27,11 @@ def _cases():
     inp = moe_synth.generate(no_local)
     inp["logits"][:, 6:8] = -1.0e4
     yield "no_local", no_local, inp
+    no_local_fp8 = moe_synth.make_config("tiny", T=256, d=256, f=256, E_global=8, k=2, e_begin=6, e_end=8,
+                                         dtype="fp8_e4m3", seed=34)
+    inp = moe_synth.generate(no_local_fp8)
+    inp["logits"][:, 6:8] = -1.0e4
+    yield "no_local_fp8", no_local_fp8, inp
     single = moe_synth.make_config("tiny", T=1, d=128, f=128, E_global=1, k=1, e_begin=0, e_end=1, seed=32)
     yield "single_token", single, moe_synth.generate(single)
     seg = moe_synth.make_config("tiny", T=8, d=256, f=128, E_global=4, k=2, e_begin=1, e_end=3, num_segments=8,
@@ -52,7 +58,7 @@ def test_degenerate_share(name, sched, tiles):
     np.testing.assert_array_equal(v["topk_idx"].numpy(), ref["topk_idx"])
     np.testing.assert_array_equal(v["tok_off"].numpy(), ref["tok_off"])
     np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
-    if name == "no_local":
+    if name.startswith("no_local"):
         assert A == 0 and int(v["meta"][1]) == 0
         assert torch.count_nonzero(Y.float()).item() == 0 and torch.count_nonzero(Y32).item() == 0
     else:

@@ -97,6 +97,18 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   __shared__ int sh[64];
   __shared__ int tot[1024];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Step 3's output-row counts of this wavefront's segment are loaded first,
+  // into registers when they fit, so their latency overlaps step 1.
+  constexpr int kRowRegs = 8;
+  const int segw = ((T + 15) / 16 + 63) / 64 * 64;
+  const int qa = min(T, w * segw), qb = min(T, qa + segw);
+  const bool rows_in_regs = segw <= 64 * kRowRegs;
+  int rc[kRowRegs];
+#pragma unroll
+  for (int u = 0; u < kRowRegs; ++u) {
+    const int q = qa + u * 64 + lane;
+    rc[u] = rows_in_regs && q < qb ? tok_cnt[q] : 0;
+  }
   for (int e = w; e < El; e += 16) {
     int run = 0;
     for (int g0 = 0; g0 < nblk; g0 += 512) {
@@ -134,13 +146,16 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     meta[META_A] = A;
   }
   // output rows: wavefront w owns a contiguous segment of q and reads it
-  // 64 consecutive rows at a time (coalesced); segment totals are scanned
-  // across the 16 wavefronts in LDS.
-  const int segw = ((T + 15) / 16 + 63) / 64 * 64;
-  const int qa = min(T, w * segw), qb = min(T, qa + segw);
+  // 64 consecutive rows at a time (coalesced), or has it in registers;
+  // segment totals are scanned across the 16 wavefronts in LDS.
   int wsum = 0;
+  if (rows_in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRowRegs; ++u) wsum += rc[u];
+  } else {
 #pragma unroll 4
-  for (int q = qa + lane; q < qb; q += 64) wsum += tok_cnt[q];
+    for (int q = qa + lane; q < qb; q += 64) wsum += tok_cnt[q];
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
   if (lane == 0) sh[32 + w] = wsum;
@@ -151,18 +166,34 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     run += i < w ? v : 0;
     total += v;
   }
-#pragma unroll 4
-  for (int q0 = qa; q0 < qb; q0 += 64) {
-    const int q = q0 + lane;
-    const int c = q < qb ? tok_cnt[q] : 0;
-    int x = c;
+  if (rows_in_regs) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
+    for (int u = 0; u < kRowRegs; ++u) {
+      const int q = qa + u * 64 + lane;
+      const int c = rc[u];
+      int x = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (q < qb) tok_off[q] = run + x - c;
+      run += __shfl(x, 63, 64);
     }
-    if (q < qb) tok_off[q] = run + x - c;
-    run += __shfl(x, 63, 64);
+  } else {
+#pragma unroll 4
+    for (int q0 = qa; q0 < qb; q0 += 64) {
+      const int q = q0 + lane;
+      const int c = q < qb ? tok_cnt[q] : 0;
+      int x = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (q < qb) tok_off[q] = run + x - c;
+      run += __shfl(x, 63, 64);
+    }
   }
   if (threadIdx.x == 0) tok_off[T] = total;
 }

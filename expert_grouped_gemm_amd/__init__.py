@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
     "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
-    "check_workspace", "tile_trace", "schedule_of", "store_burst_probe", "SCHED", "DTYPE", "STATUS",
+    "check_workspace", "tile_trace", "schedule_of", "store_burst_probe", "owner_plan", "owner_gather",
+    "segment_copy", "SCHED", "DTYPE", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,10 @@ class WorkspaceLayout(ctypes.Structure):
         "total")]
 
 
+class OwnerPlanSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("R", "bands", "remote_bands", "segments", "recv_rows")]
+
+
 _lib = None
 _P = ctypes.c_void_p
 
@@ -93,6 +98,13 @@ def lib() -> ctypes.CDLL:
         L.moe_store_burst_probe.restype = ctypes.c_int
         L.moe_store_burst_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _P,
                                             ctypes.c_size_t, _P, ctypes.c_size_t, _P]
+        L.moe_owner_plan.restype = ctypes.c_int
+        L.moe_owner_plan.argtypes = [PP, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int64, _P, _P,
+                                     _P, _P, ctypes.c_int64, _P, ctypes.POINTER(OwnerPlanSizes)]
+        L.moe_owner_gather.restype = ctypes.c_int
+        L.moe_owner_gather.argtypes = [PP, _P, _P, ctypes.c_int64, _P, _P]
+        L.moe_segment_copy.restype = ctypes.c_int
+        L.moe_segment_copy.argtypes = [PP, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]
         L.moe_schedule_of.restype = ctypes.c_int
         L.moe_schedule_of.argtypes = [PP]
         L.moe_tile_clock_hz.restype = ctypes.c_double
@@ -279,3 +291,44 @@ def layer_forward(p: Problem, X, X_scale, logits, W1, W1_scale, W2, W2_scale, Y,
 def check_workspace(p: Problem, workspace, stream=None):
     _check(lib().moe_check_workspace(ctypes.byref(p), _ptr(workspace), workspace.numel(), _stream(stream)),
            "moe_check_workspace")
+
+
+def owner_plan(p: Problem, topk_idx, local_rank: int, tb_M: int, x_bands: int) -> Dict[str, "np.ndarray"]:
+    """moe_owner_plan on host arrays: topk_idx int32 [T, k] (numpy or a CPU
+    tensor). Returns row_src, expert_off, bands [n, 5], schedule, segments
+    [n, 4], recv_start and the sizes, as numpy arrays / ints."""
+    import numpy as np
+    idx = np.ascontiguousarray(np.asarray(topk_idx, dtype=np.int32))
+    if idx.shape != (p.T, p.k):
+        raise ValueError(f"owner_plan: topk_idx shape {idx.shape}, expected {(p.T, p.k)}")
+    z = OwnerPlanSizes()
+    L = lib()
+    _check(L.moe_owner_plan(ctypes.byref(p), idx.ctypes.data, local_rank, tb_M, x_bands, None, 0, None, None, None,
+                            None, 0, None, ctypes.byref(z)), "moe_owner_plan")
+    El = p.e_end - p.e_begin
+    row_src = np.empty(max(1, z.R), np.int32)
+    expert_off = np.empty(El + 1, np.int32)
+    bands = np.empty((max(1, z.bands), 5), np.int32)
+    sched = np.empty(max(1, z.bands), np.int32)
+    segs = np.empty((max(1, z.bands), 4), np.int32)
+    recv_start = np.empty(p.num_segments + 1, np.int32)
+    _check(L.moe_owner_plan(ctypes.byref(p), idx.ctypes.data, local_rank, tb_M, x_bands, row_src.ctypes.data,
+                            row_src.shape[0], expert_off.ctypes.data, bands.ctypes.data, sched.ctypes.data,
+                            segs.ctypes.data, bands.shape[0], recv_start.ctypes.data, ctypes.byref(z)),
+           "moe_owner_plan")
+    return {"row_src": row_src[:z.R], "expert_off": expert_off, "bands": bands[:z.bands],
+            "schedule": sched[:z.bands], "segments": segs[:z.segments], "recv_start": recv_start,
+            "R": z.R, "n_bands": z.bands, "remote_bands": z.remote_bands, "n_segments": z.segments,
+            "recv_rows": z.recv_rows}
+
+
+def owner_gather(p: Problem, X, row_src, X_pad, stream=None):
+    """moe_owner_gather: X_pad[r] = X[row_src[r] // k] (zeros for -1)."""
+    _check(lib().moe_owner_gather(ctypes.byref(p), _ptr(X), _ptr(row_src), row_src.numel(), _ptr(X_pad),
+                                  _stream(stream)), "moe_owner_gather")
+
+
+def segment_copy(p: Problem, O_pad, segments, recv, stream=None):
+    """moe_segment_copy: segments int32 [n, 4] on the device."""
+    _check(lib().moe_segment_copy(ctypes.byref(p), _ptr(O_pad), O_pad.shape[0], _ptr(segments), segments.shape[0],
+                                  _ptr(recv), recv.shape[0], _stream(stream)), "moe_segment_copy")

@@ -191,6 +191,61 @@ MOE_API moe_status_t moe_store_burst_probe(int K, int B, int reps, double gap_us
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+MOE_API moe_status_t moe_owner_plan(const moe_problem_t* p, const int32_t* topk_idx, int local_rank, int tb_M,
+                                    int x_bands, int32_t* row_src, int64_t row_cap, int32_t* expert_off,
+                                    int32_t* bands, int32_t* schedule, int32_t* segments, int64_t band_cap,
+                                    int32_t* recv_start, moe_owner_plan_sizes_t* sizes) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !sizes) return MOE_ERR_INVALID_ARGUMENT;
+  if (local_rank < 0 || local_rank >= p->num_segments || tb_M < 1 || tb_M > 4096 || x_bands < 1)
+    return MOE_ERR_INVALID_ARGUMENT;
+  std::vector<int32_t> rs, eo, bd, sc, sg, rv;
+  moe::OwnerPlanSizes z = moe::owner_plan_build(*p, topk_idx, local_rank, tb_M, x_bands, rs, eo, bd, sc, sg, rv);
+  if (z.R > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  sizes->R = z.R;
+  sizes->bands = z.bands;
+  sizes->remote_bands = z.remote_bands;
+  sizes->segments = z.segments;
+  sizes->recv_rows = z.recv_rows;
+  if (!row_src && !expert_off && !bands && !schedule && !segments && !recv_start) return MOE_OK;
+  if (!row_src || !expert_off || !bands || !schedule || !segments || !recv_start) return MOE_ERR_INVALID_ARGUMENT;
+  if (row_cap < z.R || band_cap < z.bands) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  memcpy(row_src, rs.data(), rs.size() * sizeof(int32_t));
+  memcpy(expert_off, eo.data(), eo.size() * sizeof(int32_t));
+  memcpy(bands, bd.data(), bd.size() * sizeof(int32_t));
+  memcpy(schedule, sc.data(), sc.size() * sizeof(int32_t));
+  memcpy(segments, sg.data(), sg.size() * sizeof(int32_t));
+  memcpy(recv_start, rv.data(), rv.size() * sizeof(int32_t));
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const int32_t* row_src, int64_t R,
+                                      void* X_pad, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (R < 0 || R > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+  if (R > 0 && (!X || !row_src || !X_pad || !aligned16(X) || !aligned16(X_pad))) return MOE_ERR_INVALID_ARGUMENT;
+  hipError_t e = moe::launch_owner_gather(*p, X, row_src, (int)R, X_pad, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad, int64_t R,
+                                      const int32_t* segments, int64_t n_segments, float* recv, int64_t R_recv,
+                                      void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (R < 0 || R > (int64_t)INT32_MAX || R_recv < 0 || R_recv > (int64_t)INT32_MAX || n_segments < 0 ||
+      n_segments > (int64_t)INT32_MAX)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_segments > 0 && (!O_pad || !segments || !recv || !aligned16(O_pad) || !aligned16(recv)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipError_t e = moe::launch_segment_copy(*p, O_pad, (int)R, segments, (int)n_segments, recv, (int)R_recv,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 MOE_API const char* moe_status_string(moe_status_t s) {
   switch (s) {
     case MOE_OK: return "ok";

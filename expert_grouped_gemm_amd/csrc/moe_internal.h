@@ -2,6 +2,7 @@
 // constants and the kernel launchers each .hip file provides.
 #pragma once
 
+#include <vector>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -120,6 +121,20 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 
 hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
+
+// Owner-aligned return path (validated arguments; see moe_owner_plan,
+// moe_owner_gather and moe_segment_copy).
+struct OwnerPlanSizes {
+  int64_t R, bands, remote_bands, segments, recv_rows;
+};
+OwnerPlanSizes owner_plan_build(const moe_problem_t& p, const int32_t* idx, int local, int tb, int x,
+                                std::vector<int32_t>& row_src, std::vector<int32_t>& expert_off,
+                                std::vector<int32_t>& bands, std::vector<int32_t>& sched,
+                                std::vector<int32_t>& segs, std::vector<int32_t>& recv_start);
+hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const int32_t* row_src, int R, void* X_pad,
+                               hipStream_t s);
+hipError_t launch_segment_copy(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs, int n_seg,
+                               float* recv, int R_recv, hipStream_t s);
 
 // Store-burst probe (validated arguments; see moe_store_burst_probe).
 hipError_t launch_store_burst(int K, int B, int reps, double gap_us, void* buf, size_t buf_bytes, uint64_t* rec,

@@ -236,6 +236,64 @@ MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, co
 MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace, size_t ws_bytes,
                                          void* stream);
 
+/* Owner-aligned return path (Cui et al., Section 3.2.1 remote-owner-aligned
+ * row layout, Section 3.2.2 remote-first tile schedule and Algorithm 1,
+ * Section 3.2.3 combine plan, Section 3.3.2 / Figure 3b segment-granular
+ * transfer, Section 4.5 padding bound). The share's tokens belong to S =
+ * p->num_segments ranks, token t to rank t mod S; local_rank is this GPU's.
+ *
+ * moe_owner_plan (HOST pointers, no GPU call; topk_idx int32 [T, k] as from
+ * moe_route_topk, copied to the host). Inside each local expert the rows
+ * are grouped by owner rank, remote ranks ascending and local_rank last,
+ * ascending assignment id a = t*k + j inside a group; every remote group is
+ * padded with zero rows (row_src = -1) to a multiple of tb_M (1..4096), the
+ * local group is not. Outputs:
+ *   row_src    int32 [R]          assignment id of padded row r, -1 = zero row
+ *   expert_off int32 [E_l + 1]    first padded row of each expert (expert_off[E_l] = R)
+ *   bands      int32 [bands, 5]   per row band of tb_M rows (a local group's last
+ *                                 band may be shorter): local expert, owner rank,
+ *                                 first row, valid rows, row offset inside the
+ *                                 owner's receive region; in layout order
+ *   schedule   int32 [bands]      band ids, remote-first: experts by descending
+ *                                 remote band count (ties: lower expert first),
+ *                                 their remote bands, then every local band
+ *   segments   int32 [segments, 4] transfer segments: source row in the layout,
+ *                                 valid rows, destination row in the receive
+ *                                 buffer, owner rank. Per (expert, rank) group
+ *                                 the first and last segment hold one band and the
+ *                                 middle ones up to x_bands (>= 1); listed in the
+ *                                 order their first band is scheduled
+ *   recv_start int32 [S + 1]      first receive-buffer row of each rank's region;
+ *                                 a region holds its rank's rows in (expert, a) order
+ *   sizes      R, bands, remote_bands, segments, recv_rows (always filled).
+ * With every array NULL only `sizes` is filled. row_cap < R or band_cap <
+ * bands gives MOE_ERR_WORKSPACE_TOO_SMALL (sizes filled, arrays untouched);
+ * R >= 2^31 gives MOE_ERR_UNSUPPORTED. */
+typedef struct moe_owner_plan_sizes {
+  int64_t R, bands, remote_bands, segments, recv_rows;
+} moe_owner_plan_sizes_t;
+MOE_API moe_status_t moe_owner_plan(const moe_problem_t* p, const int32_t* topk_idx, int local_rank, int tb_M,
+                                    int x_bands, int32_t* row_src, int64_t row_cap, int32_t* expert_off,
+                                    int32_t* bands, int32_t* schedule, int32_t* segments, int64_t band_cap,
+                                    int32_t* recv_start, moe_owner_plan_sizes_t* sizes);
+
+/* Gather into the owner-aligned layout (bf16 only; fp8 gives
+ * MOE_ERR_UNSUPPORTED). DEVICE pointers: X bf16 [T, d], row_src int32 [R]
+ * from moe_owner_plan; X_pad bf16 [R, d] out: row r = X[row_src[r] / k], or
+ * zeros where row_src[r] is -1 (ids outside [0, T*k) also give zeros).
+ * moe_expert_forward then runs on X_pad with offsets = expert_off and
+ * row_dst[r] = r, writing the layout's expert outputs O_pad fp32 [R, d]
+ * (requires R <= T * min(k, E_l), the workspace's row capacity). */
+MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const int32_t* row_src, int64_t R,
+                                      void* X_pad, void* stream);
+
+/* Segment transfer (DEVICE pointers): for every segment (src, rows, dst, rank)
+ * of moe_owner_plan, recv[dst + i] = O_pad[src + i] for i < rows (fp32 rows of
+ * d). A segment whose rows fall outside [0, R) or [0, R_recv) is skipped. */
+MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad, int64_t R,
+                                      const int32_t* segments, int64_t n_segments, float* recv, int64_t R_recv,
+                                      void* stream);
+
 MOE_API const char* moe_status_string(moe_status_t s);
 MOE_API int moe_last_hip_error(void);
 /* Library version, e.g. "0.1.0". */

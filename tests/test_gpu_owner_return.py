@@ -57,7 +57,7 @@ SMALL = {
                                        num_segments=4, seed=21), 1, 32, 2),
     "ragged_s8": (moe_synth.make_config("tiny", T=1024, d=384, f=128, E_global=16, k=4, e_begin=5, e_end=11,
                                         num_segments=8, seed=22), 0, 16, 3),
-    "zipf_s2": (moe_synth.make_config("tiny", T=2048, d=256, f=256, E_global=16, k=2, e_begin=0, e_end=8,
+    "zipf_s2": (moe_synth.make_config("tiny", T=2048, d=256, f=256, E_global=16, k=4, e_begin=0, e_end=8,
                                       zipf_s=1.2, num_segments=2, seed=23), 1, 64, 2),
 }
 

@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--trace", action="store_true",
                     help="after the timed steps, run one call with per-tile timing and summarise the spans")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens in the oracle's timed sample")
+    ap.add_argument("--owner-return", type=int, default=0, metavar="TB_M",
+                    help="also time the owner-aligned return path (8 owner ranks, this GPU rank 0, row bands of "
+                         "TB_M rows, middle segments of 2 bands) after the timed steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy (HBM reference and counter calibration)")
     return ap.parse_args()
@@ -330,6 +333,9 @@ def main():
     if args.trace:
         out["tile_trace"] = trace_summary(moe, cfg, args, g, v)
 
+    if args.owner_return:
+        out["owner_return"] = owner_return_summary(moe, cfg, args, g, v, gemm_call_us, A)
+
     if args.copy_probe:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -349,6 +355,60 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg, g, args)
 
     print(json.dumps(out), flush=True)
+
+
+def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
+    """Owner-aligned return path (Cui et al., Sections 3.2-3.3) on this
+    workload: host plan from the routing in the workspace, padded gather,
+    the grouped GEMM on the padded layout, segment copy into the receive
+    buffer. Each device stage is timed back to back with HIP events."""
+    import torch
+    S, local, x, tb = 8, 0, 2, args.owner_return
+    p8 = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
+                          num_segments=S, sched="separate", quant_block=cfg.quant_block)
+    plan = moe.owner_plan(p8, v["topk_idx"].cpu().numpy(), local, tb, x)
+    R = plan["R"]
+    res = {"owner_ranks": S, "local_rank": local, "tb_M": tb, "x_bands": x, "A": A, "R_padded": R,
+           "padding_ratio": round(R / max(A, 1), 4), "bands": plan["n_bands"],
+           "remote_bands": plan["remote_bands"], "segments": plan["n_segments"],
+           "expert_gemm_us_unpadded": round(gemm_std_us, 2)}
+    if cfg.dtype != "bf16":
+        res["note"] = "the padded gather is bf16 only"
+        return res
+    if R > cfg.T * min(cfg.k, cfg.E_local):
+        res["note"] = "padded rows exceed the workspace row capacity T*min(k, E_l); not run"
+        return res
+    stream = torch.cuda.current_stream()
+    row_src = torch.from_numpy(plan["row_src"]).cuda()
+    X_pad = torch.empty((R, cfg.d), dtype=torch.bfloat16, device="cuda")
+    O_pad = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
+    eo = torch.from_numpy(plan["expert_off"]).cuda()
+    iota = torch.arange(R, dtype=torch.int32, device="cuda")
+    segs = torch.from_numpy(plan["segments"]).cuda().contiguous()
+    recv = torch.empty((plan["recv_rows"], cfg.d), dtype=torch.float32, device="cuda")
+    ws8 = moe.alloc_workspace(p8)
+    stages = {
+        "gather": lambda: moe.owner_gather(p8, g["X"], row_src, X_pad, stream),
+        "expert_gemm": lambda: moe.expert_forward(p8, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad,
+                                                  ws8, stream),
+        "segment_copy": lambda: moe.segment_copy(p8, O_pad, segs, recv, stream),
+    }
+    n = max(10, args.steps // 2)
+    for name, fn in stages.items():
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    moe.check_workspace(p8, ws8)
+    res["gather_GBps"] = round((A + R) * cfg.d * 2 / (res["gather_us"] * 1e-6) / 1e9, 1)
+    res["segment_copy_GBps"] = round(2 * A * cfg.d * 4 / (res["segment_copy_us"] * 1e-6) / 1e9, 1)
+    res["segment_copy_frac_hbm"] = round(res["segment_copy_GBps"] / HBM_PEAK_GBPS, 4)
+    return res
 
 
 def cpu_baseline(cfg, g, args):

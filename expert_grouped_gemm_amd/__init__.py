@@ -20,7 +20,7 @@ __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
     "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
     "check_workspace", "tile_trace", "schedule_of", "store_burst_probe", "owner_plan", "owner_gather",
-    "segment_copy", "SCHED", "DTYPE", "STATUS",
+    "segment_copy", "expert_forward_signal", "segment_copy_wait", "SCHED", "DTYPE", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +105,11 @@ def lib() -> ctypes.CDLL:
         L.moe_owner_gather.argtypes = [PP, _P, _P, ctypes.c_int64, _P, _P]
         L.moe_segment_copy.restype = ctypes.c_int
         L.moe_segment_copy.argtypes = [PP, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]
+        L.moe_expert_forward_signal.restype = ctypes.c_int
+        L.moe_expert_forward_signal.argtypes = [PP] + [_P] * 10 + [ctypes.c_int64, _P, ctypes.c_size_t, _P]
+        L.moe_segment_copy_wait.restype = ctypes.c_int
+        L.moe_segment_copy_wait.argtypes = [PP, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P,
+                                            ctypes.c_int64, _P, ctypes.c_int, _P]
         L.moe_schedule_of.restype = ctypes.c_int
         L.moe_schedule_of.argtypes = [PP]
         L.moe_tile_clock_hz.restype = ctypes.c_double
@@ -332,3 +337,20 @@ def segment_copy(p: Problem, O_pad, segments, recv, stream=None):
     """moe_segment_copy: segments int32 [n, 4] on the device."""
     _check(lib().moe_segment_copy(ctypes.byref(p), _ptr(O_pad), O_pad.shape[0], _ptr(segments), segments.shape[0],
                                   _ptr(recv), recv.shape[0], _stream(stream)), "moe_segment_copy")
+
+
+def expert_forward_signal(p: Problem, X_perm, X_perm_scale, offsets, row_dst, W1, W1_scale, W2, W2_scale,
+                          combine_buf, row_done, workspace, stream=None):
+    """moe_expert_forward_signal: also publishes stored Linear-2 elements per
+    32-row block in row_done (device int32, zeroed by the caller)."""
+    _check(lib().moe_expert_forward_signal(ctypes.byref(p), _ptr(X_perm), _ptr(X_perm_scale), _ptr(offsets),
+                                           _ptr(row_dst), _ptr(W1), _ptr(W1_scale), _ptr(W2), _ptr(W2_scale),
+                                           _ptr(combine_buf), _ptr(row_done), row_done.numel(), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "moe_expert_forward_signal")
+
+
+def segment_copy_wait(p: Problem, O_pad, segments, recv, row_done, err, grid: int = 0, stream=None):
+    """moe_segment_copy_wait: each segment waits for its rows in row_done."""
+    _check(lib().moe_segment_copy_wait(ctypes.byref(p), _ptr(O_pad), O_pad.shape[0], _ptr(segments),
+                                       segments.shape[0], _ptr(recv), recv.shape[0], _ptr(row_done),
+                                       row_done.numel(), _ptr(err), grid, _stream(stream)), "moe_segment_copy_wait")

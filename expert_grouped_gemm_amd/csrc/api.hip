@@ -246,6 +246,46 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
+                                               const float* X_perm_scale, const int32_t* offsets,
+                                               const int32_t* row_dst, const void* W1, const float* W1_scale,
+                                               const void* W2, const float* W2_scale, float* combine_buf,
+                                               int32_t* row_done, int64_t row_done_len, void* workspace,
+                                               size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (!X_perm || !offsets || !row_dst || !W1 || !W2 || !combine_buf || !row_done) return MOE_ERR_INVALID_ARGUMENT;
+  if (row_done_len < 1 || row_done_len > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_perm_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(X_perm) || !aligned16(W1) || !aligned16(W2) || !aligned16(combine_buf))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe::Layout L = moe::make_layout(*p);
+  if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
+  hipError_t e = moe::launch_expert_forward(*p, L, static_cast<char*>(workspace), X_perm, X_perm_scale, offsets,
+                                            row_dst, W1, W1_scale, W2, W2_scale, combine_buf, (hipStream_t)stream,
+                                            row_done, (int)row_done_len);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* O_pad, int64_t R,
+                                           const int32_t* segments, int64_t n_segments, float* recv,
+                                           int64_t R_recv, const int32_t* row_done, int64_t row_done_len,
+                                           int32_t* err, int grid, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (R < 0 || R > (int64_t)INT32_MAX || R_recv < 0 || R_recv > (int64_t)INT32_MAX || n_segments < 0 ||
+      n_segments > (int64_t)INT32_MAX || grid < 0 || grid > 1024 || (int64_t)p->d * 32 > (int64_t)INT32_MAX)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_segments > 0 && (!O_pad || !segments || !recv || !row_done || !err || !aligned16(O_pad) || !aligned16(recv)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_segments > 0 && row_done_len < (R + 31) / 32) return MOE_ERR_INVALID_ARGUMENT;
+  hipError_t e = moe::launch_segment_copy_wait(*p, O_pad, (int)R, segments, (int)n_segments, recv, (int)R_recv,
+                                               row_done, err, grid ? grid : 256, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 MOE_API const char* moe_status_string(moe_status_t s) {
   switch (s) {
     case MOE_OK: return "ok";

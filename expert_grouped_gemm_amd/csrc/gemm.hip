@@ -200,7 +200,8 @@ int resolve_schedule(const moe_problem_t& p) {
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, float* combine_buf, hipStream_t s) {
+                                 const float* W2_scale, float* combine_buf, hipStream_t s, int32_t* row_done,
+                                 int row_done_len) {
   const int G = gemm_grid(p);
   if (G <= 0) return hipErrorInvalidDevice;
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
@@ -238,6 +239,8 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.trace = L.pub.tile_trace_capacity ? reinterpret_cast<uint64_t*>(ws + L.pub.tile_trace) : nullptr;
   P.trace_cap = (int)L.pub.tile_trace_capacity;
   P.keep_hf = (p.flags & MOE_FLAG_KEEP_H_F32) ? 1 : 0;
+  P.row_done = row_done;
+  P.row_done_len = row_done_len;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile, K the participating workgroups and h = f, i.e.
   // the row bands one sweep of the grid covers (G / N1 here). The knee is a

@@ -98,6 +98,8 @@ struct GemmParams {
   uint64_t* trace;        // tile records of 5 words (moe_tile_record_t), or null: no timing
   int trace_cap;          // records the trace region holds
   int keep_hf;            // fp8: wide Linear-1 tiles also store their fp32 SwiGLU values in Hf
+  int32_t* row_done;      // or null: per 32-row block of output rows, output elements stored (Linear-2)
+  int row_done_len;       // blocks row_done holds
 };
 
 // Launch the persistent expert-GEMM kernel of one operand type (bf16 in
@@ -685,6 +687,27 @@ __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& 
   }
 }
 
+// After a Linear-2 tile's stores, with P.row_done set: publish the tile's
+// output elements per 32-row block of rows (row_done[b] += rows of the tile
+// in block b times its output columns). A block of the layout is complete
+// once it counts min(32, R - 32 b) * d. This is the tile-level signal of Cui
+// et al., Section 3.3.1 (a flag published after each output tile), counted
+// per row block so that a reader needs no knowledge of the tile order.
+__device__ __forceinline__ void finish_l2_tile(const GemmParams& P, const Tile& t) {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int cols = t.nnb * 64, r1 = t.row0 + t.rows;
+    for (int b = t.row0 >> 5; b <= (r1 - 1) >> 5; ++b) {
+      if (b >= P.row_done_len) break;
+      const int lo = t.row0 > (b << 5) ? t.row0 : (b << 5);
+      const int hi = r1 < (b << 5) + 32 ? r1 : (b << 5) + 32;
+      __hip_atomic_fetch_add(P.row_done + b, (hi - lo) * cols, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Tile timing (P.trace set): once every wavefront's epilogue stores (and
 // publication) are done, thread 0 takes a record slot from the device-scope
 // counter meta[META_TRACE_N] and writes the tile's four clock readings and
@@ -757,6 +780,9 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
   if (nnb == 4) dispatch_tile<4, L1, FP8>(P, t, lds, t_main);
   else dispatch_tile<2, L1, FP8>(P, t, lds, t_main);
   if constexpr (L1) finish_l1_tile<FP8>(P, t, p, fused, lds);
+  if constexpr (!L1) {
+    if (P.row_done) finish_l2_tile(P, t);
+  }
   if (P.trace) record_tile(P, L1, p, n, nnb, t_start, t_ready, t_main);
 }
 

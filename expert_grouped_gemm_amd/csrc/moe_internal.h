@@ -117,7 +117,8 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, co
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, float* combine_buf, hipStream_t s);
+                                 const float* W2_scale, float* combine_buf, hipStream_t s,
+                                 int32_t* row_done = nullptr, int row_done_len = 0);
 
 hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
@@ -135,6 +136,9 @@ hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const int3
                                hipStream_t s);
 hipError_t launch_segment_copy(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs, int n_seg,
                                float* recv, int R_recv, hipStream_t s);
+hipError_t launch_segment_copy_wait(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs,
+                                    int n_seg, float* recv, int R_recv, const int32_t* row_done, int32_t* err,
+                                    int grid, hipStream_t s);
 
 // Store-burst probe (validated arguments; see moe_store_burst_probe).
 hipError_t launch_store_burst(int K, int B, int reps, double gap_us, void* buf, size_t buf_bytes, uint64_t* rec,

@@ -60,6 +60,64 @@ __global__ __launch_bounds__(256) void segment_copy_kernel(const float* __restri
   }
 }
 
+// Segment transfer that runs beside the expert GEMM (Cui et al., Section
+// 3.3.1-3.3.3: a consumer that polls the producer's tile flags and issues
+// each segment once its tiles are stored). A small persistent grid walks the
+// segments in plan order (segment q, q + gridDim.x, ...). In every wavefront
+// lane 0 waits until every 32-row block b the segment touches counts
+// min(32, R - 32 b) * d stored elements in row_done, polling with
+// device-scope loads and a bounded spin; a timeout sets *err, and that and
+// every later segment is then skipped. The wavefront then copies its share
+// of the segment's columns. Wavefronts do not synchronise with each other:
+// each copies only what it has itself seen ready.
+//
+// The kernel uses no LDS, so it never takes LDS a GEMM workgroup needs: the
+// GEMM's persistent workgroups (the whole LDS of a CU each) stay resident
+// beside it. A segment's rows are first read after their blocks are
+// complete, rows are whole 128-byte lines (d % 128 == 0) and the launch
+// starts with the kernel-entry acquire, so neither the CU's L1 nor its XCD's
+// L2 holds a stale copy.
+__global__ __launch_bounds__(256) void segment_copy_wait_kernel(const float* __restrict__ O_pad, int R,
+                                                                const int32_t* __restrict__ seg, int n_seg,
+                                                                int R_recv, int d,
+                                                                const int32_t* __restrict__ row_done,
+                                                                int32_t* __restrict__ err,
+                                                                float* __restrict__ recv) {
+  const int lane = threadIdx.x & 63;
+  const int vec = d >> 2;
+  for (int q = blockIdx.x; q < n_seg; q += gridDim.x) {
+    const int* s = seg + 4 * q;
+    const int src = s[0], n = s[1], dst = s[2];
+    if (src < 0 || n <= 0 || dst < 0 || src > R - n || dst > R_recv - n) continue;
+    int ok = 1;
+    if (lane == 0) {
+      for (int b = src >> 5; ok && b <= (src + n - 1) >> 5; ++b) {
+        const int need = (R - (b << 5) < 32 ? R - (b << 5) : 32) * d;
+        int spins = 0;
+        while (__hip_atomic_load(row_done + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(64);  // about 2 us between polls: little issue and memory traffic beside the GEMM
+          if (++spins > kSpinLimit) {
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    ok = __shfl(ok, 0, 64);
+    if (!ok) continue;
+    for (int i = 0; i < n; ++i) {
+      const float4* a = reinterpret_cast<const float4*>(O_pad + (size_t)(src + i) * d);
+      float4* b = reinterpret_cast<float4*>(recv + (size_t)(dst + i) * d);
+      for (int c = threadIdx.x; c < vec; c += blockDim.x) b[c] = a[c];
+    }
+  }
+}
+
 }  // namespace
 
 OwnerPlanSizes owner_plan_build(const moe_problem_t& p, const int32_t* idx, int local, int tb, int x,
@@ -160,6 +218,16 @@ hipError_t launch_segment_copy(const moe_problem_t& p, const float* O_pad, int R
                                float* recv, int R_recv, hipStream_t s) {
   if (n_seg == 0) return hipSuccess;
   hipLaunchKernelGGL(segment_copy_kernel, dim3(n_seg, 16), dim3(256), 0, s, O_pad, R, segs, R_recv, p.d, recv);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_copy_wait(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs,
+                                    int n_seg, float* recv, int R_recv, const int32_t* row_done, int32_t* err,
+                                    int grid, hipStream_t s) {
+  if (n_seg == 0) return hipSuccess;
+  const int g = grid < n_seg ? grid : n_seg;
+  hipLaunchKernelGGL(segment_copy_wait_kernel, dim3(g), dim3(256), 0, s, O_pad, R, segs, n_seg, R_recv, p.d,
+                     row_done, err, recv);
   return hipGetLastError();
 }
 

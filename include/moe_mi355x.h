@@ -294,6 +294,36 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
                                       const int32_t* segments, int64_t n_segments, float* recv, int64_t R_recv,
                                       void* stream);
 
+/* Overlapped segment transfer (Cui et al., Section 3.3.1 tile-level signaling
+ * and Section 3.3.3 producer-consumer co-scheduling, on one GPU).
+ *
+ * moe_expert_forward_signal: moe_expert_forward that also publishes, after
+ * every Linear-2 tile's stores, the tile's output elements per 32-row block
+ * of rows: row_done[b] += (rows of the tile in block b) * (its columns),
+ * after a device-scope release. Block b of an R-row layout is complete at
+ * min(32, R - 32 b) * d. row_done: DEVICE int32 [row_done_len], zero at the
+ * call (the caller clears it), at least ceil(R / 32) blocks; counts past
+ * row_done_len are dropped.
+ *
+ * moe_segment_copy_wait: moe_segment_copy whose segments each wait until
+ * their rows' blocks are complete in row_done (ceil(R / 32) <= row_done_len),
+ * so it can run on a second stream beside moe_expert_forward_signal (launch
+ * it after the clearing of row_done is ordered before it). grid persistent
+ * workgroups (1..1024; 0 = 256, one per compute unit) walk the segments in plan order; they use no
+ * LDS, so the GEMM's workgroups stay resident beside them. Waits are
+ * bounded: a timeout (about a second) sets *err (DEVICE int32, zero at the
+ * call) to 1, and that and every later segment are skipped. */
+MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
+                                               const float* X_perm_scale, const int32_t* offsets,
+                                               const int32_t* row_dst, const void* W1, const float* W1_scale,
+                                               const void* W2, const float* W2_scale, float* combine_buf,
+                                               int32_t* row_done, int64_t row_done_len, void* workspace,
+                                               size_t ws_bytes, void* stream);
+MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* O_pad, int64_t R,
+                                           const int32_t* segments, int64_t n_segments, float* recv,
+                                           int64_t R_recv, const int32_t* row_done, int64_t row_done_len,
+                                           int32_t* err, int grid, void* stream);
+
 MOE_API const char* moe_status_string(moe_status_t s);
 MOE_API int moe_last_hip_error(void);
 /* Library version, e.g. "0.1.0". */

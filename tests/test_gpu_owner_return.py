@@ -116,3 +116,88 @@ def test_owner_return_deepseek_share_full_size():
     order = a_loc[key]
     want = np.stack([fused[int(a)] for a in order])
     np.testing.assert_array_equal(got, want)
+
+
+def _overlapped(p, X, g, plan, ws, grid=0):
+    """Gather, then the signalling GEMM on the launch stream and the waiting
+    segment copier on a second stream (default priority), started together."""
+    R = plan["R"]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    row_src = torch.from_numpy(plan["row_src"]).cuda()
+    X_pad = torch.empty((R, p.d), dtype=torch.bfloat16, device="cuda")
+    O_pad = torch.full((R, p.d), float("nan"), dtype=torch.float32, device="cuda")
+    recv = torch.full((plan["recv_rows"], p.d), float("nan"), dtype=torch.float32, device="cuda")
+    row_done = torch.zeros((R + 31) // 32, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    segs = torch.from_numpy(plan["segments"]).cuda().contiguous()
+    eo = torch.from_numpy(plan["expert_off"]).cuda()
+    iota = torch.arange(R, dtype=torch.int32, device="cuda")
+    moe.owner_gather(p, X, row_src, X_pad, main)
+    ev = torch.cuda.Event()
+    ev.record(main)
+    side.wait_event(ev)
+    moe.segment_copy_wait(p, O_pad, segs, recv, row_done, err, grid, stream=side)
+    moe.expert_forward_signal(p, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad, row_done, ws,
+                              stream=main)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    return recv, int(err.item()), row_done
+
+
+@pytest.mark.parametrize("name", ["share_s4", "ragged_s8"])
+def test_overlapped_copy_matches_stream_ordered(name):
+    cfg, local, tb, x = SMALL[name]
+    print(f"overlapped owner return {name}", flush=True)
+    inp = moe_synth.generate(cfg)
+    g = to_gpu(inp)
+    p = problem_of(cfg, sched="separate")
+    _, _, ws = run_layer(p, g)
+    idx = moe.workspace_views(p, ws)["topk_idx"].cpu().numpy()
+    plan = moe.owner_plan(p, idx, local, tb, x)
+    ws2 = moe.alloc_workspace(p)
+    # two calls in a row, the second on other token values (no stale rows may be copied)
+    X2 = moe_synth.generate(cfg, seed=cfg.seed + 100)["X"].cuda()
+    for X in (g["X"], X2):
+        g2 = dict(g, X=X)
+        want = _owner_return(p, g2, idx, local, tb, x)[2].cpu().numpy()
+        recv, err, row_done = _overlapped(p, X, g, plan, ws2, grid=8)
+        assert err == 0
+        R = plan["R"]
+        full = np.minimum(32, R - 32 * np.arange(len(row_done))) * p.d
+        np.testing.assert_array_equal(row_done.cpu().numpy(), full)
+        np.testing.assert_array_equal(recv.cpu().numpy(), want)
+
+
+def test_overlapped_copy_deepseek_share_full_size():
+    cfg = moe_synth.make_config("deepseek_share_bf16", num_segments=8)
+    print("overlapped owner return deepseek_share_bf16 S=8 local=0 tb=32 x=2", flush=True)
+    g = moe_synth.generate(cfg, device="cuda")
+    p = problem_of(cfg, sched="separate")
+    _, _, ws = run_layer(p, g)
+    idx = moe.workspace_views(p, ws)["topk_idx"].cpu().numpy()
+    plan, _, want = _owner_return(p, g, idx, 0, 32, 2)
+    recv, err, _ = _overlapped(p, g["X"], g, plan, moe.alloc_workspace(p))
+    assert err == 0
+    torch.testing.assert_close(recv, want, rtol=0, atol=0)
+
+
+def test_copier_wait_timeout_is_reported():
+    # No GEMM runs, so no block is ever complete: the first segment's bounded
+    # wait gives up, sets the error word, and every segment is skipped.
+    cfg, local, tb, x = SMALL["share_s4"]
+    print("copier timeout path", flush=True)
+    p = problem_of(cfg, sched="separate")
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, cfg.E_global, size=(cfg.T, cfg.k)).astype(np.int32)
+    plan = moe.owner_plan(p, idx, local, tb, x)
+    R = plan["R"]
+    O_pad = torch.zeros((R, p.d), dtype=torch.float32, device="cuda")
+    recv = torch.full((plan["recv_rows"], p.d), float("nan"), dtype=torch.float32, device="cuda")
+    row_done = torch.zeros((R + 31) // 32, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    segs = torch.from_numpy(plan["segments"]).cuda().contiguous()
+    moe.segment_copy_wait(p, O_pad, segs, recv, row_done, err, grid=4)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert torch.isnan(recv).all()

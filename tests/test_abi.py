@@ -143,3 +143,24 @@ def test_store_burst_probe_rejects_bad_arguments(L):
         assert call(**over) == 1, over
     assert L.moe_store_burst_probe(4, 4096, 3, ctypes.c_double(1.0), None, ctypes.c_size_t(1 << 20), fake,
                                    ctypes.c_size_t(1 << 20), None) == 1
+
+
+def test_binding_argument_counts_match_the_header(L):
+    # Every declared entry point the binding describes takes as many
+    # arguments in its ctypes signature as the header declares.
+    src = ""
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src += open(os.path.join(ROOT, "include", fn)).read()
+    decls = re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(([^;]*?)\)\s*;", src, flags=re.S)
+    assert decls
+    checked = 0
+    for name, params in decls:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        argtypes = getattr(L, name).argtypes
+        if argtypes is None:
+            continue
+        assert len(argtypes) == n, (name, len(argtypes), n)
+        checked += 1
+    assert checked >= 15

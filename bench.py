@@ -372,15 +372,15 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
            "padding_ratio": round(R / max(A, 1), 4), "bands": plan["n_bands"],
            "remote_bands": plan["remote_bands"], "segments": plan["n_segments"],
            "expert_gemm_us_unpadded": round(gemm_std_us, 2)}
-    if cfg.dtype != "bf16":
-        res["note"] = "the padded gather is bf16 only"
-        return res
-    if R > cfg.T * min(cfg.k, cfg.E_local):
+    fp8 = cfg.dtype == "fp8_e4m3"
+    cap = cfg.T * min(cfg.k, cfg.E_local)
+    if R > cap:
         res["note"] = "padded rows exceed the workspace row capacity T*min(k, E_l); not run"
         return res
     stream = torch.cuda.current_stream()
     row_src = torch.from_numpy(plan["row_src"]).cuda()
-    X_pad = torch.empty((R, cfg.d), dtype=torch.bfloat16, device="cuda")
+    X_pad = torch.empty((R, cfg.d), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    X_pad_scale = torch.empty((cfg.d // 128, cap), dtype=torch.float32, device="cuda") if fp8 else None
     O_pad = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
     eo = torch.from_numpy(plan["expert_off"]).cuda()
     iota = torch.arange(R, dtype=torch.int32, device="cuda")
@@ -388,9 +388,9 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
     recv = torch.empty((plan["recv_rows"], cfg.d), dtype=torch.float32, device="cuda")
     ws8 = moe.alloc_workspace(p8)
     stages = {
-        "gather": lambda: moe.owner_gather(p8, g["X"], row_src, X_pad, stream),
-        "expert_gemm": lambda: moe.expert_forward(p8, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad,
-                                                  ws8, stream),
+        "gather": lambda: moe.owner_gather(p8, g["X"], g.get("X_scale"), row_src, X_pad, X_pad_scale, stream),
+        "expert_gemm": lambda: moe.expert_forward(p8, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"),
+                                                  g["W2"], g.get("W2_scale"), O_pad, ws8, stream),
         "segment_copy": lambda: moe.segment_copy(p8, O_pad, segs, recv, stream),
     }
     n = max(10, args.steps // 2)
@@ -405,6 +405,13 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         torch.cuda.synchronize()
         res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
     moe.check_workspace(p8, ws8)
+    res["gather_GBps"] = round((A + R) * cfg.d * (1 if fp8 else 2) / (res["gather_us"] * 1e-6) / 1e9, 1)
+    res["segment_copy_GBps"] = round(2 * A * cfg.d * 4 / (res["segment_copy_us"] * 1e-6) / 1e9, 1)
+    res["segment_copy_frac_hbm"] = round(res["segment_copy_GBps"] / HBM_PEAK_GBPS, 4)
+    if fp8:
+        res["overlap_note"] = ("not run: the fp8 GEMM's wavefronts take a SIMD's whole register file, so the "
+                               "waiting copier cannot share a compute unit with it")
+        return res
     # Overlap (Cui et al., Section 3.3): the signalling GEMM on the launch
     # stream and the waiting copier on a second stream, against the same two
     # stages run one after the other.
@@ -420,16 +427,16 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
 
     def gemm_signal():
         row_done.zero_()
-        moe.expert_forward_signal(p8b, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad, row_done, ws8,
-                                  stream)
+        moe.expert_forward_signal(p8b, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
+                                  g.get("W2_scale"), O_pad, row_done, ws8, stream)
 
     def overlapped():
         row_done.zero_()
         ev.record(stream)
         side.wait_event(ev)
         moe.segment_copy_wait(p8, O_pad, segs, recv, row_done, err, 0, side)
-        moe.expert_forward_signal(p8b, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad, row_done, ws8,
-                                  stream)
+        moe.expert_forward_signal(p8b, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
+                                  g.get("W2_scale"), O_pad, row_done, ws8, stream)
         stream.wait_stream(side)
 
     def sequential():
@@ -452,7 +459,7 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
     res["overlap_ratio"] = round((res["sequential_us"] - res["overlapped_us"]) / res["segment_copy_us"], 3)
     res["overlap_note"] = ("overlap_ratio = (sequential - overlapped) / segment_copy: the share of the copy "
                            "hidden under the GEMM (the signalling GEMM's own cost included)")
-    res["gather_GBps"] = round((A + R) * cfg.d * 2 / (res["gather_us"] * 1e-6) / 1e9, 1)
+    res["gather_GBps"] = round((A + R) * cfg.d * (1 if fp8 else 2) / (res["gather_us"] * 1e-6) / 1e9, 1)
     res["segment_copy_GBps"] = round(2 * A * cfg.d * 4 / (res["segment_copy_us"] * 1e-6) / 1e9, 1)
     res["segment_copy_frac_hbm"] = round(res["segment_copy_GBps"] / HBM_PEAK_GBPS, 4)
     return res

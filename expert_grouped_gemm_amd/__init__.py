@@ -102,7 +102,7 @@ def lib() -> ctypes.CDLL:
         L.moe_owner_plan.argtypes = [PP, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int64, _P, _P,
                                      _P, _P, ctypes.c_int64, _P, ctypes.POINTER(OwnerPlanSizes)]
         L.moe_owner_gather.restype = ctypes.c_int
-        L.moe_owner_gather.argtypes = [PP, _P, _P, ctypes.c_int64, _P, _P]
+        L.moe_owner_gather.argtypes = [PP, _P, _P, _P, ctypes.c_int64, _P, _P, _P]
         L.moe_segment_copy.restype = ctypes.c_int
         L.moe_segment_copy.argtypes = [PP, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]
         L.moe_expert_forward_signal.restype = ctypes.c_int
@@ -327,10 +327,11 @@ def owner_plan(p: Problem, topk_idx, local_rank: int, tb_M: int, x_bands: int) -
             "recv_rows": z.recv_rows}
 
 
-def owner_gather(p: Problem, X, row_src, X_pad, stream=None):
-    """moe_owner_gather: X_pad[r] = X[row_src[r] // k] (zeros for -1)."""
-    _check(lib().moe_owner_gather(ctypes.byref(p), _ptr(X), _ptr(row_src), row_src.numel(), _ptr(X_pad),
-                                  _stream(stream)), "moe_owner_gather")
+def owner_gather(p: Problem, X, X_scale, row_src, X_pad, X_pad_scale=None, stream=None):
+    """moe_owner_gather: X_pad[r] = X[row_src[r] // k] (zeros for -1); fp8
+    also the row scales into X_pad_scale [d/128, T*min(k, E_l)]."""
+    _check(lib().moe_owner_gather(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(row_src), row_src.numel(),
+                                  _ptr(X_pad), _ptr(X_pad_scale), _stream(stream)), "moe_owner_gather")
 
 
 def segment_copy(p: Problem, O_pad, segments, recv, stream=None):

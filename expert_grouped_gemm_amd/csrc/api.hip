@@ -220,14 +220,20 @@ MOE_API moe_status_t moe_owner_plan(const moe_problem_t* p, const int32_t* topk_
   return MOE_OK;
 }
 
-MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const int32_t* row_src, int64_t R,
-                                      void* X_pad, void* stream) {
+MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const float* X_scale,
+                                      const int32_t* row_src, int64_t R, void* X_pad, float* X_pad_scale,
+                                      void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const int64_t El = p->e_end - p->e_begin;
+  const int64_t cap = (int64_t)p->T * (p->k < El ? p->k : El);
   if (R < 0 || R > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_scale != nullptr) || fp8 != (X_pad_scale != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 && R > cap) return MOE_ERR_UNSUPPORTED;  // the scale rows are laid out with the workspace's capacity
   if (R > 0 && (!X || !row_src || !X_pad || !aligned16(X) || !aligned16(X_pad))) return MOE_ERR_INVALID_ARGUMENT;
-  hipError_t e = moe::launch_owner_gather(*p, X, row_src, (int)R, X_pad, (hipStream_t)stream);
+  hipError_t e = moe::launch_owner_gather(*p, X, X_scale, row_src, (int)R, X_pad, X_pad_scale, (int)cap,
+                                          (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -281,6 +287,10 @@ MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* 
   if (n_segments > 0 && (!O_pad || !segments || !recv || !row_done || !err || !aligned16(O_pad) || !aligned16(recv)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (n_segments > 0 && row_done_len < (R + 31) / 32) return MOE_ERR_INVALID_ARGUMENT;
+  // The fp8 GEMM's wavefronts take a SIMD's whole register file (256 VGPRs,
+  // two per SIMD), so no copier wavefront can share a CU with its workgroups:
+  // every wait would time out.
+  if (p->dtype == MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
   hipError_t e = moe::launch_segment_copy_wait(*p, O_pad, (int)R, segments, (int)n_segments, recv, (int)R_recv,
                                                row_done, err, grid ? grid : 256, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);

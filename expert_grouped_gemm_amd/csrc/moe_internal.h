@@ -132,8 +132,8 @@ OwnerPlanSizes owner_plan_build(const moe_problem_t& p, const int32_t* idx, int 
                                 std::vector<int32_t>& row_src, std::vector<int32_t>& expert_off,
                                 std::vector<int32_t>& bands, std::vector<int32_t>& sched,
                                 std::vector<int32_t>& segs, std::vector<int32_t>& recv_start);
-hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const int32_t* row_src, int R, void* X_pad,
-                               hipStream_t s);
+hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const float* X_scale, const int32_t* row_src,
+                               int R, void* X_pad, float* X_pad_scale, int cap, hipStream_t s);
 hipError_t launch_segment_copy(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs, int n_seg,
                                float* recv, int R_recv, hipStream_t s);
 hipError_t launch_segment_copy_wait(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs,

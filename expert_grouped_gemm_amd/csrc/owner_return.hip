@@ -43,6 +43,27 @@ __global__ __launch_bounds__(256) void owner_gather_kernel(const uint16_t* __res
   }
 }
 
+// fp8: the e4m3 codes of X[row_src[r] / k] (16 bytes per lane) and the row's
+// block scales, X_pad_scale[c * cap + r] = X_scale[t / 128][c] (the K-block-
+// major layout the grouped GEMM reads); a zero row gets codes 0 and scale 1.
+__global__ __launch_bounds__(256) void owner_gather_fp8_kernel(const uint8_t* __restrict__ X,
+                                                               const float* __restrict__ Xs,
+                                                               const int32_t* __restrict__ row_src, int R, int Tk,
+                                                               int k, int d, int cap, uint8_t* __restrict__ X_pad,
+                                                               float* __restrict__ X_pad_scale) {
+  const int vec = d >> 4, db = d >> 7;
+  for (int r = blockIdx.x; r < R; r += gridDim.x) {
+    const int a = row_src[r];
+    const bool valid = a >= 0 && a < Tk;
+    const int t = valid ? a / k : 0;
+    uint4* dst = reinterpret_cast<uint4*>(X_pad + (size_t)r * d);
+    const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)t * d);
+    for (int c = threadIdx.x; c < vec; c += blockDim.x) dst[c] = valid ? src[c] : make_uint4(0, 0, 0, 0);
+    for (int c = threadIdx.x; c < db; c += blockDim.x)
+      X_pad_scale[(size_t)c * cap + r] = valid ? Xs[(size_t)(t >> 7) * db + c] : 1.0f;
+  }
+}
+
 // One segment per blockIdx.x; blockIdx.y strides its rows. A segment is
 // (src row, rows, dst row, dest); one whose rows fall outside [0, R) or
 // [0, R_recv) is skipped.
@@ -205,10 +226,15 @@ OwnerPlanSizes owner_plan_build(const moe_problem_t& p, const int32_t* idx, int 
   return z;
 }
 
-hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const int32_t* row_src, int R, void* X_pad,
-                               hipStream_t s) {
+hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const float* X_scale, const int32_t* row_src,
+                               int R, void* X_pad, float* X_pad_scale, int cap, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int blocks = R < 8192 ? R : 8192;
+  if (p.dtype == MOE_DTYPE_FP8_E4M3) {
+    hipLaunchKernelGGL(owner_gather_fp8_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(X),
+                       X_scale, row_src, R, p.T * p.k, p.k, p.d, cap, static_cast<uint8_t*>(X_pad), X_pad_scale);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(owner_gather_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(X), row_src,
                      R, p.T * p.k, p.k, p.d, static_cast<uint16_t*>(X_pad));
   return hipGetLastError();

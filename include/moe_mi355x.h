@@ -277,15 +277,19 @@ MOE_API moe_status_t moe_owner_plan(const moe_problem_t* p, const int32_t* topk_
                                     int32_t* bands, int32_t* schedule, int32_t* segments, int64_t band_cap,
                                     int32_t* recv_start, moe_owner_plan_sizes_t* sizes);
 
-/* Gather into the owner-aligned layout (bf16 only; fp8 gives
- * MOE_ERR_UNSUPPORTED). DEVICE pointers: X bf16 [T, d], row_src int32 [R]
- * from moe_owner_plan; X_pad bf16 [R, d] out: row r = X[row_src[r] / k], or
- * zeros where row_src[r] is -1 (ids outside [0, T*k) also give zeros).
- * moe_expert_forward then runs on X_pad with offsets = expert_off and
- * row_dst[r] = r, writing the layout's expert outputs O_pad fp32 [R, d]
- * (requires R <= T * min(k, E_l), the workspace's row capacity). */
-MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const int32_t* row_src, int64_t R,
-                                      void* X_pad, void* stream);
+/* Gather into the owner-aligned layout. DEVICE pointers: X [T, d] (bf16, or
+ * e4m3 codes with X_scale fp32 [T/128, d/128]; X_scale must be NULL for
+ * bf16), row_src int32 [R] from moe_owner_plan. X_pad [R, d] out: row r =
+ * X[row_src[r] / k], or zeros where row_src[r] is -1 (ids outside [0, T*k)
+ * also give zeros). fp8: X_pad_scale fp32 [d/128, cap] out, cap = T *
+ * min(k, E_l): row r's block scales at c * cap + r (the layout
+ * moe_expert_forward reads; 1 for a zero row); R > cap gives
+ * MOE_ERR_UNSUPPORTED. moe_expert_forward then runs on X_pad with offsets =
+ * expert_off and row_dst[r] = r, writing the layout's expert outputs O_pad
+ * fp32 [R, d] (requires R <= cap, the workspace's row capacity). */
+MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const float* X_scale,
+                                      const int32_t* row_src, int64_t R, void* X_pad, float* X_pad_scale,
+                                      void* stream);
 
 /* Segment transfer (DEVICE pointers): for every segment (src, rows, dst, rank)
  * of moe_owner_plan, recv[dst + i] = O_pad[src + i] for i < rows (fp32 rows of
@@ -312,7 +316,9 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
  * workgroups (1..1024; 0 = 256, one per compute unit) walk the segments in plan order; they use no
  * LDS, so the GEMM's workgroups stay resident beside them. Waits are
  * bounded: a timeout (about a second) sets *err (DEVICE int32, zero at the
- * call) to 1, and that and every later segment are skipped. */
+ * call) to 1, and that and every later segment are skipped. fp8 problems
+ * give MOE_ERR_UNSUPPORTED: the fp8 GEMM's wavefronts take a SIMD's whole
+ * register file, so no copier wavefront can run beside its workgroups. */
 MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
                                                const float* X_perm_scale, const int32_t* offsets,
                                                const int32_t* row_dst, const void* W1, const float* W1_scale,

@@ -28,12 +28,15 @@ def _owner_return(p, g, idx, local, tb, x):
     cap = p.T * min(p.k, El)
     assert R <= cap, f"padded rows {R} exceed the workspace row capacity {cap}"
     row_src = torch.from_numpy(plan["row_src"]).cuda()
-    X_pad = torch.empty((R, p.d), dtype=torch.bfloat16, device="cuda")
-    moe.owner_gather(p, g["X"], row_src, X_pad)
+    fp8 = p.dtype == moe.DTYPE["fp8_e4m3"]
+    X_pad = torch.empty((R, p.d), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    X_pad_scale = torch.empty((p.d // 128, cap), dtype=torch.float32, device="cuda") if fp8 else None
+    moe.owner_gather(p, g["X"], g.get("X_scale"), row_src, X_pad, X_pad_scale)
     O_pad = torch.empty((R, p.d), dtype=torch.float32, device="cuda")
     ws = moe.alloc_workspace(p)
-    moe.expert_forward(p, X_pad, None, torch.from_numpy(plan["expert_off"]).cuda(),
-                       torch.arange(R, dtype=torch.int32, device="cuda"), g["W1"], None, g["W2"], None, O_pad, ws)
+    moe.expert_forward(p, X_pad, X_pad_scale, torch.from_numpy(plan["expert_off"]).cuda(),
+                       torch.arange(R, dtype=torch.int32, device="cuda"), g["W1"], g.get("W1_scale"), g["W2"],
+                       g.get("W2_scale"), O_pad, ws)
     recv = torch.full((plan["recv_rows"], p.d), float("nan"), dtype=torch.float32, device="cuda")
     moe.segment_copy(p, O_pad, torch.from_numpy(plan["segments"]).cuda().contiguous(), recv)
     torch.cuda.synchronize()
@@ -133,7 +136,7 @@ def _overlapped(p, X, g, plan, ws, grid=0):
     segs = torch.from_numpy(plan["segments"]).cuda().contiguous()
     eo = torch.from_numpy(plan["expert_off"]).cuda()
     iota = torch.arange(R, dtype=torch.int32, device="cuda")
-    moe.owner_gather(p, X, row_src, X_pad, main)
+    moe.owner_gather(p, X, None, row_src, X_pad, None, main)
     ev = torch.cuda.Event()
     ev.record(main)
     side.wait_event(ev)
@@ -201,3 +204,53 @@ def test_copier_wait_timeout_is_reported():
     torch.cuda.synchronize()
     assert int(err.item()) == 1
     assert torch.isnan(recv).all()
+
+
+def test_owner_return_fp8():
+    # e4m3 codes with 128x128 block scales: padded codes and row scales
+    # bit-exact, receive buffer bit-exact against the fused fp8 path.
+    cfg = moe_synth.make_config("tiny", T=512, d=256, f=256, E_global=8, k=4, e_begin=0, e_end=4,
+                                dtype="fp8_e4m3", num_segments=4, seed=24)
+    print("owner return fp8 small S=4 local=2 tb=32 x=2", flush=True)
+    inp = moe_synth.generate(cfg)
+    g = to_gpu(inp)
+    p = problem_of(cfg, sched="separate")
+    _, _, ws = run_layer(p, g)
+    fused, idx = _fused_outputs_by_assignment(p, ws)
+    plan = moe.owner_plan(p, idx, 2, 32, 2)
+    R, cap = plan["R"], cfg.cap
+    assert R <= cap
+    row_src = torch.from_numpy(plan["row_src"]).cuda()
+    X_pad = torch.empty((R, p.d), dtype=torch.uint8, device="cuda")
+    X_pad_scale = torch.full((p.d // 128, cap), -7.0, dtype=torch.float32, device="cuda")
+    moe.owner_gather(p, g["X"], g["X_scale"], row_src, X_pad, X_pad_scale)
+    torch.cuda.synchronize()
+    rs = plan["row_src"]
+    xs = inp["X"].numpy()
+    sc = inp["X_scale"].numpy()
+    got_x = X_pad.cpu().numpy()
+    np.testing.assert_array_equal(got_x[rs >= 0], xs[rs[rs >= 0] // cfg.k])
+    assert not np.any(got_x[rs < 0])
+    got_s = X_pad_scale.cpu().numpy()
+    tok = np.maximum(rs, 0) // cfg.k
+    want_s = np.where(rs[None, :] >= 0, sc[tok // 128].T, 1.0)
+    np.testing.assert_array_equal(got_s[:, :R], want_s)
+    assert np.all(got_s[:, R:] == -7.0)
+    plan2, _, recv = _owner_return(p, g, idx, 2, 32, 2)
+    want = ol.segment_return(idx, cfg.e_begin, cfg.e_end, cfg.num_segments, lambda a: fused[a])
+    np.testing.assert_array_equal(recv.cpu().numpy(), want)
+
+
+def test_owner_return_fp8_deepseek_share_full_size():
+    cfg = moe_synth.CONFIGS["deepseek_share_fp8"]
+    print("owner return deepseek_share_fp8 S=8 local=0 tb=32 x=2", flush=True)
+    g = moe_synth.generate(cfg, device="cuda")
+    p = problem_of(cfg, sched="separate")
+    _, _, ws = run_layer(p, g)
+    fused, idx = _fused_outputs_by_assignment(p, ws)
+    plan, _, recv = _owner_return(p, g, idx, 0, 32, 2)
+    flat = idx.reshape(-1)
+    a_loc = np.nonzero((flat >= cfg.e_begin) & (flat < cfg.e_end))[0]
+    order = a_loc[np.lexsort((a_loc, flat[a_loc], (a_loc // cfg.k) % 8))]
+    want = np.stack([fused[int(a)] for a in order])
+    np.testing.assert_array_equal(recv.cpu().numpy(), want)

@@ -78,5 +78,10 @@ def test_plan_sizes_only_and_errors():
         assert L.moe_owner_plan(ctypes.byref(p), a.ctypes.data, local, tb, x, None, 0, None, None, None, None, 0,
                                 None, ctypes.byref(z)) == 1
     pf = moe.make_problem(128, 128, 128, E, k, 0, 8, num_segments=4, dtype="fp8_e4m3")
-    assert L.moe_owner_gather(ctypes.byref(pf), 16, 16, 1, 16, None) == 2   # bf16 only
+    assert L.moe_owner_gather(ctypes.byref(pf), 16, None, 16, 1, 16, None, None) == 1   # fp8 needs scales
+    assert L.moe_owner_gather(ctypes.byref(p), 16, 16, 16, 1, 16, None, None) == 1      # bf16 takes none
+    cap = 128 * 2
+    assert L.moe_owner_gather(ctypes.byref(pf), 16, 16, 16, cap + 1, 16, 16, None) == 2  # fp8 rows beyond cap
     assert L.moe_segment_copy(ctypes.byref(p), None, 4, None, 1, None, 4, None) == 1
+    rd = np.zeros(4, np.int32)
+    assert L.moe_segment_copy_wait(ctypes.byref(pf), 16, 64, 16, 1, 16, 64, rd.ctypes.data, 4, 16, 0, None) == 2

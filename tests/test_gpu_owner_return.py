@@ -254,3 +254,32 @@ def test_owner_return_fp8_deepseek_share_full_size():
     order = a_loc[np.lexsort((a_loc, flat[a_loc], (a_loc // cfg.k) % 8))]
     want = np.stack([fused[int(a)] for a in order])
     np.testing.assert_array_equal(recv.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("sched", ["separate", "expert_wave", "interleaved"])
+def test_signal_counts_every_output_element(sched):
+    # In every schedule (including the interleaved tail of narrow Linear-2
+    # tiles), the signalling GEMM counts each stored output element once per
+    # 32-row block, and writes the same rows as the plain GEMM.
+    cfg = moe_synth.make_config("tiny", T=1000, d=384, f=384, E_global=16, k=4, e_begin=3, e_end=11,
+                                num_segments=4, seed=25)
+    print(f"signal counts {sched}", flush=True)
+    g = to_gpu(moe_synth.generate(cfg))
+    p = problem_of(cfg, sched=sched)
+    _, _, ws = run_layer(p, g)
+    v = moe.workspace_views(p, ws)
+    A = int(v["meta"][0].item())
+    R = A
+    iota = torch.arange(max(R, 1), dtype=torch.int32, device="cuda")
+    O_plain = torch.full((R, p.d), float("nan"), dtype=torch.float32, device="cuda")
+    O_sig = torch.full((R, p.d), float("nan"), dtype=torch.float32, device="cuda")
+    row_done = torch.zeros((R + 31) // 32, dtype=torch.int32, device="cuda")
+    ws2 = moe.alloc_workspace(p)
+    moe.expert_forward(p, v["x_perm"], None, v["offsets"], iota, g["W1"], None, g["W2"], None, O_plain, ws2)
+    moe.expert_forward_signal(p, v["x_perm"], None, v["offsets"], iota, g["W1"], None, g["W2"], None, O_sig,
+                              row_done, ws2)
+    torch.cuda.synchronize()
+    moe.check_workspace(p, ws2)
+    full = np.minimum(32, R - 32 * np.arange(len(row_done))) * p.d
+    np.testing.assert_array_equal(row_done.cpu().numpy(), full)
+    torch.testing.assert_close(O_sig, O_plain, rtol=0, atol=0)

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void owner_gather_fp8_kernel(const uint8_t* __
   }
 }
 
-// One segment per blockIdx.x; blockIdx.y strides its rows. A segment is
+// One segment per blockIdx.x; blockIdx.y (32 of them) strides its rows, so a
+// segment of up to 32 rows has a workgroup per row. A segment is
 // (src row, rows, dst row, dest); one whose rows fall outside [0, R) or
 // [0, R_recv) is skipped.
 __global__ __launch_bounds__(256) void segment_copy_kernel(const float* __restrict__ O_pad, int R,
@@ -243,7 +244,7 @@ hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const floa
 hipError_t launch_segment_copy(const moe_problem_t& p, const float* O_pad, int R, const int32_t* segs, int n_seg,
                                float* recv, int R_recv, hipStream_t s) {
   if (n_seg == 0) return hipSuccess;
-  hipLaunchKernelGGL(segment_copy_kernel, dim3(n_seg, 16), dim3(256), 0, s, O_pad, R, segs, R_recv, p.d, recv);
+  hipLaunchKernelGGL(segment_copy_kernel, dim3(n_seg, 32), dim3(256), 0, s, O_pad, R, segs, R_recv, p.d, recv);
   return hipGetLastError();
 }
 

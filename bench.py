@@ -16,10 +16,12 @@ Default workload: the DeepSeek-style share (T=4096 tokens, d=7168, f=2048,
 top-8 of 256 experts, this GPU owns experts 0-31, bf16). Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--sched auto|interleaved|expert_wave|separate]
-                  [--no-cpu-baseline] [--no-compare] [--trace] [--copy-probe]
+                  [--no-cpu-baseline] [--no-compare] [--trace] [--copy-probe] [--owner-return TB_M]
 
 After the main measurement the same steps are timed under each explicit
-schedule (schedules_TFLOPs), unless --no-compare.
+schedule (schedules_TFLOPs), unless --no-compare. --owner-return adds the
+owner-aligned return path's stages (padded gather, GEMM on the padded layout,
+segment copy, and for bf16 the overlapped copy) as an "owner_return" object.
 """
 from __future__ import annotations
 

@@ -441,11 +441,22 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
                                   g.get("W2_scale"), O_pad, row_done, ws8, stream)
         stream.wait_stream(side)
 
+    def overlapped_raster():
+        # the same pair with the GEMM's default (grouped raster) tile order
+        row_done.zero_()
+        ev.record(stream)
+        side.wait_event(ev)
+        moe.segment_copy_wait(p8, O_pad, segs, recv, row_done, err, 0, side)
+        moe.expert_forward_signal(p8, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
+                                  g.get("W2_scale"), O_pad, row_done, ws8, stream)
+        stream.wait_stream(side)
+
     def sequential():
         stages["expert_gemm"]()
         stages["segment_copy"]()
 
-    for name, fn in (("expert_gemm_signal", gemm_signal), ("sequential", sequential), ("overlapped", overlapped)):
+    for name, fn in (("expert_gemm_signal", gemm_signal), ("sequential", sequential), ("overlapped", overlapped),
+                     ("overlapped_raster_order", overlapped_raster)):
         for _ in range(5):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -370,15 +370,13 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
                           num_segments=S, sched="separate", quant_block=cfg.quant_block)
     plan = moe.owner_plan(p8, v["topk_idx"].cpu().numpy(), local, tb, x)
     R = plan["R"]
+    p8.row_capacity = max(R, moe.row_capacity(p8))  # the workspace holds the padded rows
     res = {"owner_ranks": S, "local_rank": local, "tb_M": tb, "x_bands": x, "A": A, "R_padded": R,
            "padding_ratio": round(R / max(A, 1), 4), "bands": plan["n_bands"],
            "remote_bands": plan["remote_bands"], "segments": plan["n_segments"],
            "expert_gemm_us_unpadded": round(gemm_std_us, 2)}
     fp8 = cfg.dtype == "fp8_e4m3"
-    cap = cfg.T * min(cfg.k, cfg.E_local)
-    if R > cap:
-        res["note"] = "padded rows exceed the workspace row capacity T*min(k, E_l); not run"
-        return res
+    cap = moe.row_capacity(p8)
     stream = torch.cuda.current_stream()
     row_src = torch.from_numpy(plan["row_src"]).cuda()
     X_pad = torch.empty((R, cfg.d), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
@@ -425,8 +423,11 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
     # the signalling GEMM walks its tile lists band by band, so that bands
     # complete one after another while the Linear-2 launch runs
     p8b = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
-                           num_segments=S, sched="separate", quant_block=cfg.quant_block, band_major=True)
+                           num_segments=S, sched="separate", quant_block=cfg.quant_block, band_major=True,
+                           row_capacity=p8.row_capacity)
 
+    # Every variant clears row_done first, so that the four carry the same
+    # extra work; the copier's error word is checked after each.
     def gemm_signal():
         row_done.zero_()
         moe.expert_forward_signal(p8b, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
@@ -436,7 +437,7 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         row_done.zero_()
         ev.record(stream)
         side.wait_event(ev)
-        moe.segment_copy_wait(p8, O_pad, segs, recv, row_done, err, 0, side)
+        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
         moe.expert_forward_signal(p8b, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
                                   g.get("W2_scale"), O_pad, row_done, ws8, stream)
         stream.wait_stream(side)
@@ -446,12 +447,13 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         row_done.zero_()
         ev.record(stream)
         side.wait_event(ev)
-        moe.segment_copy_wait(p8, O_pad, segs, recv, row_done, err, 0, side)
+        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
         moe.expert_forward_signal(p8, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
                                   g.get("W2_scale"), O_pad, row_done, ws8, stream)
         stream.wait_stream(side)
 
     def sequential():
+        row_done.zero_()
         stages["expert_gemm"]()
         stages["segment_copy"]()
 
@@ -466,8 +468,8 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         e1.record(stream)
         torch.cuda.synchronize()
         res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
-    if int(err.item()) != 0:
-        raise RuntimeError("moe_segment_copy_wait: a readiness wait timed out")
+        if int(err.item()) != 0:
+            raise RuntimeError(f"moe_segment_copy_wait: a readiness wait timed out ({name})")
     moe.check_workspace(p8, ws8)
     res["overlap_ratio"] = round((res["sequential_us"] - res["overlapped_us"]) / res["segment_copy_us"], 3)
     res["overlap_note"] = ("overlap_ratio = (sequential - overlapped) / segment_copy: the share of the copy "

@@ -28,14 +28,16 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
           4: "MOE_ERR_HIP", 5: "MOE_ERR_DEADLOCK"}
-SCHED = {"separate": 0, "expert_wave": 1, "interleaved": 2, "auto": 3}
+SCHED = {"expert_wave": 0, "interleaved": 1, "separate": 2, "auto": 3}
 DTYPE = {"bf16": 0, "fp8_e4m3": 1}
 # MOE_FLAG_* of moe_mi355x.h
-TILE_FLAGS = {"auto": 0, "narrow": 1, "wide": 2}
-FLAG_BAND_MAJOR = 4
-FLAG_TILE_TRACE = 8
-FLAG_KEEP_H_F32 = 16
-FLAG_TEST_WAIT_TIMEOUT = 32
+FLAG_FP32_Y_DEBUG = 1 << 0
+FLAG_BF16_COMBINE_BUF = 1 << 1
+TILE_FLAGS = {"auto": 0, "narrow": 1 << 2, "wide": 1 << 3}
+FLAG_BAND_MAJOR = 1 << 4
+FLAG_TILE_TRACE = 1 << 5
+FLAG_KEEP_H_F32 = 1 << 6
+FLAG_TEST_WAIT_TIMEOUT = 1 << 7
 
 
 class MoEError(RuntimeError):
@@ -50,7 +52,7 @@ class MoEError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d", "f", "E_global", "k", "e_begin", "e_end", "dtype", "quant_block", "num_segments", "sched",
-        "lead_D", "wave_experts", "grid")] + [("flags", ctypes.c_uint32)]
+        "lead_D", "wave_experts", "grid")] + [("flags", ctypes.c_uint32), ("row_capacity", ctypes.c_int32)]
 
     def __repr__(self):
         return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [PP, _P, _P, _P, _P, _P, _P]
         L.moe_layer_forward.restype = ctypes.c_int
-        L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.moe_layer_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t] + [_P] * 6
         L.moe_check_workspace.restype = ctypes.c_int
         L.moe_check_workspace.argtypes = [PP, _P, ctypes.c_size_t, _P]
         L.moe_store_burst_probe.restype = ctypes.c_int
@@ -127,17 +129,28 @@ def lib() -> ctypes.CDLL:
 def make_problem(T: int, d: int, f: int, E_global: int, k: int, e_begin: int = 0, e_end: Optional[int] = None,
                  dtype: str = "bf16", num_segments: int = 1, sched: str = "interleaved", lead_D: int = 0,
                  wave_experts: int = 0, grid: int = 0, quant_block: int = 128, tiles: str = "auto",
-                 band_major: bool = False, trace: bool = False, keep_h_f32: bool = False) -> Problem:
+                 band_major: bool = False, trace: bool = False, keep_h_f32: bool = False,
+                 bf16_combine_buf: bool = False, fp32_y: bool = False, row_capacity: int = 0) -> Problem:
     """tiles: "auto" (chosen from the shape), "narrow" or "wide" expert-GEMM tiles;
     band_major: walk the separate / expert-wave tile lists band by band;
     trace: record one timed span per expert-GEMM tile (read with tile_trace);
-    keep_h_f32: fp8, store every fp32 SwiGLU value in the workspace view h_f32."""
+    keep_h_f32: fp8, store every fp32 SwiGLU value in the workspace view h_f32;
+    bf16_combine_buf: the combine buffer holds bf16 rows (MOE_FLAG_BF16_COMBINE_BUF);
+    fp32_y: MOE_FLAG_FP32_Y_DEBUG (layer_forward then requires Y_fp32);
+    row_capacity: rows the workspace holds for the expert GEMM (0: T * min(k, E_l))."""
     flags = (TILE_FLAGS[tiles] | (FLAG_BAND_MAJOR if band_major else 0) | (FLAG_TILE_TRACE if trace else 0)
-             | (FLAG_KEEP_H_F32 if keep_h_f32 else 0))
+             | (FLAG_KEEP_H_F32 if keep_h_f32 else 0) | (FLAG_BF16_COMBINE_BUF if bf16_combine_buf else 0)
+             | (FLAG_FP32_Y_DEBUG if fp32_y else 0))
     return Problem(T=T, d=d, f=f, E_global=E_global, k=k, e_begin=e_begin,
                    e_end=E_global if e_end is None else e_end, dtype=DTYPE[dtype], quant_block=quant_block,
                    num_segments=num_segments, sched=SCHED[sched], lead_D=lead_D, wave_experts=wave_experts,
-                   grid=grid, flags=flags)
+                   grid=grid, flags=flags, row_capacity=row_capacity)
+
+
+def row_capacity(p: Problem) -> int:
+    """Rows the workspace holds for the expert GEMM (the library's rule)."""
+    El = p.e_end - p.e_begin
+    return max(p.T * min(p.k, El), p.row_capacity)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -184,9 +197,10 @@ def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
     """Typed views of the intermediates a moe_layer_forward call leaves in `ws`."""
     L = workspace_layout(p)
     El = p.e_end - p.e_begin
-    cap = p.T * min(p.k, El)
+    cap = row_capacity(p)
     esz = 1 if p.dtype == DTYPE["fp8_e4m3"] else 2
     edt = torch.uint8 if esz == 1 else torch.bfloat16
+    cb_dt = torch.bfloat16 if p.flags & FLAG_BF16_COMBINE_BUF else torch.float32
 
     def view(off, n, dt, shape):
         nbytes = n * torch.empty((), dtype=dt).element_size()
@@ -203,7 +217,7 @@ def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
         comb_w=view(L.comb_w, cap, torch.float32, (cap,)),
         x_perm=view(L.x_perm, cap * p.d, edt, (cap, p.d)),
         h=view(L.h, cap * p.f, edt, (cap, p.f)),
-        combine_buf=view(L.combine_buf, cap * p.d, torch.float32, (cap, p.d)),
+        combine_buf=view(L.combine_buf, cap * p.d, cb_dt, (cap, p.d)),
         meta=view(L.meta, 64, torch.int32, (64,)),
     )
     if esz == 1:
@@ -287,10 +301,20 @@ def combine(p: Problem, combine_buf, tok_off, comb_w, Y, Y_fp32=None, stream=Non
                              _stream(stream)), "moe_combine")
 
 
-def layer_forward(p: Problem, X, X_scale, logits, W1, W1_scale, W2, W2_scale, Y, Y_fp32, workspace, stream=None):
+def layer_forward(p: Problem, X, X_scale, logits, W1, W1_scale, W2, W2_scale, Y, Y_fp32, workspace, stream=None,
+                  topk_idx=None, topk_w=None, counts=None, offsets=None, row_src=None):
+    """moe_layer_forward. The optional outputs (device int32 / fp32 tensors of
+    shapes [T, k], [T, k], [E_l], [E_l + 1], [row capacity]) receive the
+    routing and dispatch results in place of their workspace regions."""
+    El = p.e_end - p.e_begin
+    for name, t, n in (("topk_idx", topk_idx, p.T * p.k), ("topk_w", topk_w, p.T * p.k), ("counts", counts, El),
+                       ("offsets", offsets, El + 1), ("row_src", row_src, row_capacity(p))):
+        if t is not None and t.numel() < n:
+            raise ValueError(f"layer_forward: {name} holds {t.numel()} elements, needs {n}")
     _check(lib().moe_layer_forward(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(logits), _ptr(W1), _ptr(W1_scale),
                                    _ptr(W2), _ptr(W2_scale), _ptr(Y), _ptr(Y_fp32), _ptr(workspace),
-                                   workspace.numel(), _stream(stream)), "moe_layer_forward")
+                                   workspace.numel(), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                                   _ptr(row_src), _stream(stream)), "moe_layer_forward")
 
 
 def check_workspace(p: Problem, workspace, stream=None):
@@ -329,7 +353,7 @@ def owner_plan(p: Problem, topk_idx, local_rank: int, tb_M: int, x_bands: int) -
 
 def owner_gather(p: Problem, X, X_scale, row_src, X_pad, X_pad_scale=None, stream=None):
     """moe_owner_gather: X_pad[r] = X[row_src[r] // k] (zeros for -1); fp8
-    also the row scales into X_pad_scale [d/128, T*min(k, E_l)]."""
+    also the row scales into X_pad_scale [d/128, row capacity]."""
     _check(lib().moe_owner_gather(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(row_src), row_src.numel(),
                                   _ptr(X_pad), _ptr(X_pad_scale), _stream(stream)), "moe_owner_gather")
 
@@ -350,8 +374,12 @@ def expert_forward_signal(p: Problem, X_perm, X_perm_scale, offsets, row_dst, W1
                                            workspace.numel(), _stream(stream)), "moe_expert_forward_signal")
 
 
-def segment_copy_wait(p: Problem, O_pad, segments, recv, row_done, err, grid: int = 0, stream=None):
-    """moe_segment_copy_wait: each segment waits for its rows in row_done."""
-    _check(lib().moe_segment_copy_wait(ctypes.byref(p), _ptr(O_pad), O_pad.shape[0], _ptr(segments),
+def segment_copy_wait(p: Problem, O_pad, R: int, segments, recv, row_done, err, grid: int = 0, stream=None):
+    """moe_segment_copy_wait: each segment waits for its rows in row_done. R is
+    the layout's row count (the plan's expert_off[E_l]), which sets the last
+    row block's target; O_pad must hold at least R rows."""
+    if O_pad.shape[0] < R:
+        raise ValueError(f"segment_copy_wait: O_pad holds {O_pad.shape[0]} rows, the layout has {R}")
+    _check(lib().moe_segment_copy_wait(ctypes.byref(p), _ptr(O_pad), R, _ptr(segments),
                                        segments.shape[0], _ptr(recv), recv.shape[0], _ptr(row_done),
                                        row_done.numel(), _ptr(err), grid, _stream(stream)), "moe_segment_copy_wait")

@@ -5,6 +5,12 @@
 
 #include "moe_internal.h"
 
+namespace moe {
+const void* gemm_kernel_bf16();
+const void* gemm_kernel_fp8();
+const void* segment_copy_wait_kernel_ptr();
+}  // namespace moe
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -17,19 +23,19 @@ moe_status_t hip_fail(hipError_t e) {
 moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
   if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_AUTO) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->flags & ~(uint32_t)(MOE_FLAG_TILE_NARROW | MOE_FLAG_TILE_WIDE | MOE_FLAG_BAND_MAJOR | MOE_FLAG_TILE_TRACE |
-                                MOE_FLAG_KEEP_H_F32 | MOE_FLAG_TEST_WAIT_TIMEOUT))
+  if (p->sched < MOE_SCHED_EXPERT_WAVE || p->sched > MOE_SCHED_AUTO) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->flags & ~(uint32_t)(MOE_FLAG_FP32_Y_DEBUG | MOE_FLAG_BF16_COMBINE_BUF | MOE_FLAG_TILE_NARROW |
+                                MOE_FLAG_TILE_WIDE | MOE_FLAG_BAND_MAJOR | MOE_FLAG_TILE_TRACE | MOE_FLAG_KEEP_H_F32 |
+                                MOE_FLAG_TEST_WAIT_TIMEOUT))
     return MOE_ERR_INVALID_ARGUMENT;
   if ((p->flags & MOE_FLAG_TILE_NARROW) && (p->flags & MOE_FLAG_TILE_WIDE)) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->lead_D < 0 || p->wave_experts < 0 || p->grid < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->lead_D < 0 || p->wave_experts < 0 || p->grid < 0 || p->row_capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (p->T < 1 || p->d < 1 || p->f < 1 || p->E_global < 1 || p->k < 1) return MOE_ERR_UNSUPPORTED;
   if (p->E_global > 1024 || p->k > 16 || p->k > p->E_global) return MOE_ERR_UNSUPPORTED;
   if (p->e_begin < 0 || p->e_begin >= p->e_end || p->e_end > p->E_global) return MOE_ERR_UNSUPPORTED;
   if (p->num_segments < 1 || p->T % p->num_segments) return MOE_ERR_UNSUPPORTED;
   if (p->d % 128 || p->f % 128) return MOE_ERR_UNSUPPORTED;
-  const int64_t El = p->e_end - p->e_begin;
-  const int64_t cap = (int64_t)p->T * (p->k < El ? p->k : El);
+  const int64_t cap = moe::row_capacity(*p);
   // 32-bit row and element indices inside the kernels
   if ((int64_t)p->T * p->k > (1ll << 30) || cap * p->d > (1ll << 31) - 1 || cap * p->f > (1ll << 31) - 1)
     return MOE_ERR_UNSUPPORTED;
@@ -47,6 +53,19 @@ moe_status_t check_ws(const moe::Layout& L, const void* ws, size_t bytes) {
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
+// Whether a copier wavefront fits on a SIMD beside the expert GEMM's
+// wavefronts (two per SIMD): their register counts, as the runtime reports
+// them, rounded up to the allocation granule of 8, within the 512 registers
+// per lane of a SIMD.
+bool copier_fits_beside_gemm(bool fp8) {
+  hipFuncAttributes g{}, c{};
+  if (hipFuncGetAttributes(&g, fp8 ? moe::gemm_kernel_fp8() : moe::gemm_kernel_bf16()) != hipSuccess) return false;
+  if (hipFuncGetAttributes(&c, moe::segment_copy_wait_kernel_ptr()) != hipSuccess) return false;
+  auto granule = [](int r) { return (r + 7) / 8 * 8; };
+  const int waves_per_simd = moe::gemm_threads(fp8) / 64 / 4;
+  return waves_per_simd * granule(g.numRegs) + granule(c.numRegs) <= 512;
+}
 
 }  // namespace
 
@@ -98,7 +117,7 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
 MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
                                         const int32_t* offsets, const int32_t* row_dst, const void* W1,
                                         const float* W1_scale, const void* W2, const float* W2_scale,
-                                        float* combine_buf, void* workspace, size_t ws_bytes, void* stream) {
+                                        void* combine_buf, void* workspace, size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
@@ -115,7 +134,7 @@ MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_pe
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-MOE_API moe_status_t moe_combine(const moe_problem_t* p, const float* combine_buf, const int32_t* tok_off,
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf, const int32_t* tok_off,
                                  const float* comb_w, void* Y, float* Y_fp32, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
@@ -128,15 +147,21 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const float* combine_bu
 MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
                                        const float* logits, const void* W1, const float* W1_scale,
                                        const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
-                                       void* workspace, size_t ws_bytes, void* stream) {
+                                       void* workspace, size_t ws_bytes, int32_t* topk_idx_out,
+                                       float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                       int32_t* row_src_out, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
   if (!X || !logits || !W1 || !W2 || !Y) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
+  if ((p->flags & MOE_FLAG_FP32_Y_DEBUG) && !Y_fp32) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y) || (Y_fp32 && !aligned16(Y_fp32)))
     return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* q : {(const void*)topk_idx_out, (const void*)topk_w_out, (const void*)counts_out,
+                        (const void*)offsets_out, (const void*)row_src_out})
+    if (q && (reinterpret_cast<uintptr_t>(q) & 3)) return MOE_ERR_INVALID_ARGUMENT;
   moe::Layout L = moe::make_layout(*p);
   if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
   char* ws = static_cast<char*>(workspace);
@@ -144,15 +169,20 @@ MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, co
   auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const moe_workspace_layout_t& W = L.pub;
-  hipError_t e = moe::launch_route(*p, logits, I(W.topk_idx), F(W.topk_w), nullptr, s);
+  // a caller's output takes the place of its workspace region
+  int32_t* idx = topk_idx_out ? topk_idx_out : I(W.topk_idx);
+  float* wts = topk_w_out ? topk_w_out : F(W.topk_w);
+  int32_t* counts = counts_out ? counts_out : I(W.counts);
+  int32_t* offsets = offsets_out ? offsets_out : I(W.offsets);
+  int32_t* row_src = row_src_out ? row_src_out : I(W.row_src);
+  hipError_t e = moe::launch_route(*p, logits, idx, wts, nullptr, s);
   if (e == hipSuccess)
-    e = moe::launch_dispatch(*p, L, ws, X, X_scale, I(W.topk_idx), F(W.topk_w), I(W.counts), I(W.offsets),
-                             I(W.row_src), I(W.row_dst), I(W.tok_off), F(W.comb_w), ws + W.x_perm,
-                             fp8 ? F(W.x_perm_scale) : nullptr, s);
+    e = moe::launch_dispatch(*p, L, ws, X, X_scale, idx, wts, counts, offsets, row_src, I(W.row_dst), I(W.tok_off),
+                             F(W.comb_w), ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, s);
   if (e == hipSuccess)
-    e = moe::launch_expert_forward(*p, L, ws, ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, I(W.offsets),
-                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, F(W.combine_buf), s);
-  if (e == hipSuccess) e = moe::launch_combine(*p, F(W.combine_buf), I(W.tok_off), F(W.comb_w), Y, Y_fp32, s);
+    e = moe::launch_expert_forward(*p, L, ws, ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, offsets,
+                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, ws + W.combine_buf, s);
+  if (e == hipSuccess) e = moe::launch_combine(*p, ws + W.combine_buf, I(W.tok_off), F(W.comb_w), Y, Y_fp32, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -163,17 +193,19 @@ MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace
   moe::Layout L = moe::make_layout(*p);
   if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.pub.meta) + moe::META_ERR;
-  int32_t host = 0;
-  hipError_t e = hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, s);
+  int32_t* meta = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.pub.meta);
+  int32_t host[moe::META_ARG_ERR + 1] = {};
+  hipError_t e = hipMemcpyAsync(host, meta, sizeof(host), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
-  if (host) {
+  const bool timed_out = host[moe::META_ERR] != 0, bad_arg = host[moe::META_ARG_ERR] != 0;
+  if (timed_out || bad_arg) {
     const int32_t zero = 0;
-    e = hipMemcpyAsync(flag, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(meta + moe::META_ERR, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(meta + moe::META_ARG_ERR, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e);
-    return MOE_ERR_DEADLOCK;
+    return timed_out ? MOE_ERR_DEADLOCK : MOE_ERR_INVALID_ARGUMENT;
   }
   return MOE_OK;
 }
@@ -226,8 +258,7 @@ MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, con
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
-  const int64_t El = p->e_end - p->e_begin;
-  const int64_t cap = (int64_t)p->T * (p->k < El ? p->k : El);
+  const int64_t cap = moe::row_capacity(*p);
   if (R < 0 || R > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_scale != nullptr) || fp8 != (X_pad_scale != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 && R > cap) return MOE_ERR_UNSUPPORTED;  // the scale rows are laid out with the workspace's capacity
@@ -255,7 +286,7 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
 MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
                                                const float* X_perm_scale, const int32_t* offsets,
                                                const int32_t* row_dst, const void* W1, const float* W1_scale,
-                                               const void* W2, const float* W2_scale, float* combine_buf,
+                                               const void* W2, const float* W2_scale, void* combine_buf,
                                                int32_t* row_done, int64_t row_done_len, void* workspace,
                                                size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
@@ -287,10 +318,9 @@ MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* 
   if (n_segments > 0 && (!O_pad || !segments || !recv || !row_done || !err || !aligned16(O_pad) || !aligned16(recv)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (n_segments > 0 && row_done_len < (R + 31) / 32) return MOE_ERR_INVALID_ARGUMENT;
-  // The fp8 GEMM's wavefronts take a SIMD's whole register file (256 VGPRs,
-  // two per SIMD), so no copier wavefront can share a CU with its workgroups:
-  // every wait would time out.
-  if (p->dtype == MOE_DTYPE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  // A copier wavefront must fit on a SIMD beside the GEMM's two (the fp8
+  // GEMM's take the whole register file): otherwise every wait would time out.
+  if (!copier_fits_beside_gemm(p->dtype == MOE_DTYPE_FP8_E4M3)) return MOE_ERR_UNSUPPORTED;
   hipError_t e = moe::launch_segment_copy_wait(*p, O_pad, (int)R, segments, (int)n_segments, recv, (int)R_recv,
                                                row_done, err, grid ? grid : 256, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
@@ -313,7 +343,7 @@ MOE_API int moe_last_hip_error(void) { return g_last_hip_error; }
 MOE_API const char* moe_version(void) { return "0.1.0"; }
 
 MOE_API int moe_schedule_of(const moe_problem_t* p) {
-  if (!p || p->sched < MOE_SCHED_SEPARATE || p->sched > MOE_SCHED_AUTO) return -1;
+  if (!p || p->sched < MOE_SCHED_EXPERT_WAVE || p->sched > MOE_SCHED_AUTO) return -1;
   return moe::resolve_schedule(*p);
 }
 

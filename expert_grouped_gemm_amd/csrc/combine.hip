@@ -7,36 +7,55 @@
 // Y[q] = sum_{p in [tok_off[q], tok_off[q+1])} comb_w[p] * combine_buf[p],
 // in ascending slot order, fp32 fused multiply-add, rounded once to bf16.
 // Deterministic: each output element is owned by one lane, no atomics.
-// Streaming: every lane moves 32 contiguous bytes of fp32 per slot and
-// stores 16 bytes of bf16; one workgroup per output row at a time.
+// Streaming: every lane moves 8 contiguous columns per slot (32 bytes of
+// fp32, or 16 of bf16 with a bf16 buffer) and stores 16 bytes of bf16; one
+// workgroup per output row at a time.
+// The slot range comes from device memory (a caller's tok_off): a range that
+// does not lie inside [0, cap) gives a NaN row and reads nothing.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ buf,
+template <bool BF16_IN>
+__device__ __forceinline__ void load8(const void* buf, size_t row, int d, int c, float (&v)[8]) {
+  if constexpr (BF16_IN) {
+    const uint4 u = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(buf) + row * d)[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(buf) + row * d) + 2 * c;
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool BF16_IN>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ buf,
                                                       const int32_t* __restrict__ tok_off,
-                                                      const float* __restrict__ comb_w, int T, int d,
+                                                      const float* __restrict__ comb_w, int T, int d, int cap,
                                                       uint16_t* __restrict__ Y, float* __restrict__ Y32) {
   const int vec = d >> 3;  // 8 columns per lane-step
   for (int q = blockIdx.x; q < T; q += gridDim.x) {
     const int p0 = tok_off[q], p1 = tok_off[q + 1];
+    const bool ok = 0 <= p0 && p0 <= p1 && p1 <= cap;
     for (int c = threadIdx.x; c < vec; c += blockDim.x) {
       float acc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int p = p0; p < p1; ++p) {
-        const float wgt = comb_w[p];
-        const float4* src = reinterpret_cast<const float4*>(buf + (size_t)p * d) + 2 * c;
-        const float4 u = src[0], v = src[1];
-        acc[0] = fmaf(wgt, u.x, acc[0]);
-        acc[1] = fmaf(wgt, u.y, acc[1]);
-        acc[2] = fmaf(wgt, u.z, acc[2]);
-        acc[3] = fmaf(wgt, u.w, acc[3]);
-        acc[4] = fmaf(wgt, v.x, acc[4]);
-        acc[5] = fmaf(wgt, v.y, acc[5]);
-        acc[6] = fmaf(wgt, v.z, acc[6]);
-        acc[7] = fmaf(wgt, v.w, acc[7]);
+      for (int i = 0; i < 8; ++i) acc[i] = ok ? 0.0f : __builtin_nanf("");
+      if (ok) {
+        for (int p = p0; p < p1; ++p) {
+          const float wgt = comb_w[p];
+          float v[8];
+          load8<BF16_IN>(buf, (size_t)p, d, c, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+        }
       }
       uint4 o;
       o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
@@ -55,11 +74,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
+hipError_t launch_combine(const moe_problem_t& p, const void* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s) {
   const int blocks = p.T < 8192 ? p.T : 8192;
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, combine_buf, tok_off, comb_w, p.T, p.d,
-                     static_cast<uint16_t*>(Y), Y_fp32);
+  const int cap = (int)row_capacity(p);
+  if (p.flags & MOE_FLAG_BF16_COMBINE_BUF)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, combine_buf, tok_off, comb_w, p.T, p.d,
+                       cap, static_cast<uint16_t*>(Y), Y_fp32);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, combine_buf, tok_off, comb_w, p.T,
+                       p.d, cap, static_cast<uint16_t*>(Y), Y_fp32);
   return hipGetLastError();
 }
 

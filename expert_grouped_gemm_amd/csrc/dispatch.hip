@@ -28,8 +28,12 @@ namespace {
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                              int S, int chunk, int e_begin, int El, int nblk,
                                                              int32_t* __restrict__ blk_counts,
-                                                             int32_t* __restrict__ tok_cnt) {
+                                                             int32_t* __restrict__ tok_cnt,
+                                                             int32_t* __restrict__ meta) {
   const int Tk = T * k;
+  if (blockIdx.x == 0 && threadIdx.x == 0)  // this call's capacity check starts clear
+    __hip_atomic_fetch_and(meta + META_ARG_ERR, ~(int)ARG_ERR_DISPATCH_CAP, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   extern __shared__ int32_t hist_all[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x * 4 + w;
@@ -87,8 +91,12 @@ __device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
 // loaded together): exclusive prefix of its chunk counts, in place, and the
 // expert total. (2) offsets = exclusive scan of the totals; A. (3) tok_off:
 // exclusive scan of the local-slot counts of the output rows.
+// A routing whose local assignments exceed the row capacity (a caller's
+// topk_idx that lists an expert twice for one token) sets the capacity error
+// bit and A = 0: the scatter then stores only what fits, the gather nothing,
+// and the expert GEMM's own check of the offsets stops it.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tok_cnt, int T, int El,
-                                                             int nblk,
+                                                             int nblk, int cap,
                                                              int32_t* __restrict__ blk_counts,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
@@ -143,7 +151,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   }
   if (e == 0) {
     offsets[El] = A;
-    meta[META_A] = A;
+    meta[META_A] = A <= cap ? A : 0;
+    if (A > cap)
+      __hip_atomic_fetch_or(meta + META_ARG_ERR, (int)ARG_ERR_DISPATCH_CAP, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
   }
   // output rows: wavefront w owns a contiguous segment of q and reads it
   // 64 consecutive rows at a time (coalesced), or has it in registers;
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
 // base of each expert (offset + chunk prefix) from LDS.
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
                                                               const float* __restrict__ w, int T, int k, int S,
-                                                              int chunk, int e_begin, int El, int nblk,
+                                                              int chunk, int e_begin, int El, int nblk, int cap,
                                                               const int32_t* __restrict__ blk_prefix,
                                                               const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ tok_off,
@@ -243,9 +254,11 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
       for (int jj = 0; jj < 16; ++jj)
         if (jj < j) before += (unsigned)(idx[(size_t)t * k + jj] - e_begin) < (unsigned)El;
       const int slot = tok_off[y_row_of_token(t, T, S)] + before;
-      row_src[pos] = a;
-      row_dst[pos] = slot;
-      comb_w[slot] = w[a];
+      if (pos < cap) {  // only a routing past the capacity (reported by the scan) fails these
+        row_src[pos] = a;
+        row_dst[pos] = slot;
+      }
+      if (slot < cap) comb_w[slot] = w[a];
     }
   }
 }
@@ -284,15 +297,15 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, co
   int32_t* meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
   int32_t* tok_cnt = reinterpret_cast<int32_t*>(ws + L.tok_cnt);
   hipLaunchKernelGGL(dispatch_count_kernel, dim3((L.nblk + 3) / 4), dim3(256), 4 * El * 4, s, idx, p.T, p.k,
-                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, tok_cnt);
+                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, tok_cnt, meta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, tok_cnt, p.T, El, L.nblk, blk, counts,
-                     offsets, tok_off, meta);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, tok_cnt, p.T, El, L.nblk, L.cap, blk,
+                     counts, offsets, tok_off, meta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nblk), dim3(64), El * 4, s, idx, w, p.T, p.k,
-                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, offsets, tok_off, row_src, row_dst,
-                     comb_w);
+                     p.num_segments, L.chunk, p.e_begin, El, L.nblk, L.cap, blk, offsets, tok_off, row_src,
+                     row_dst, comb_w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
   const int row_bytes = p.d * (fp8 ? 1 : 2);

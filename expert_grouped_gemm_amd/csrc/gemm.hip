@@ -10,8 +10,12 @@ namespace {
 // Row bands from the per-expert offsets, zeroed l2_full counters, and the
 // expert waves (fewest consecutive experts whose Linear-1 tiles reach the grid,
 // or a fixed number of experts per wave).
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int N1, int G,
-                                                    int wave_experts, int sort_bands, int Pmax,
+// The offsets come from device memory the host never sees (a caller's, or
+// the dispatch's): unless they are non-decreasing with 0 <= offsets[0] and
+// offsets[E_l] <= cap, the plan has no band, so no tile runs and nothing is
+// stored, and the error bit is set for moe_check_workspace.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int cap, int N1,
+                                                    int G, int wave_experts, int sort_bands, int Pmax,
                                                     int32_t* __restrict__ blk_done,
                                                     int nblk_done, int32_t* __restrict__ band_expert,
                                                     int32_t* __restrict__ band_row0,
@@ -24,12 +28,26 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (threadIdx.x == 0) {
     meta[META_ERR] = 0;  // the flag reports this call only
     meta[META_TRACE_N] = 0;
+    __hip_atomic_fetch_and(meta + META_ARG_ERR, ~(int)(ARG_ERR_OFFSETS | ARG_ERR_ROW_DST), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
   const int e = threadIdx.x;
   int cnt = 0, nb = 0;
+  bool bad = false;
   if (e < El) {
-    cnt = offsets[e + 1] - offsets[e];
+    const int lo = offsets[e], hi = offsets[e + 1];
+    cnt = hi - lo;
+    bad = cnt < 0 || (e == 0 && lo < 0) || (e == El - 1 && hi > cap);
     nb = (cnt + kBM - 1) / kBM;
+  }
+  if (__syncthreads_or(bad)) {
+    if (threadIdx.x == 0) {
+      meta[META_P] = 0;
+      meta[META_A] = 0;
+      meta[META_NWAVES] = 0;
+      __hip_atomic_fetch_or(meta + META_ARG_ERR, (int)ARG_ERR_OFFSETS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
   }
   // block exclusive scan of nb
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -200,7 +218,7 @@ int resolve_schedule(const moe_problem_t& p) {
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, float* combine_buf, hipStream_t s, int32_t* row_done,
+                                 const float* W2_scale, void* combine_buf, hipStream_t s, int32_t* row_done,
                                  int row_done_len) {
   const int G = gemm_grid(p);
   if (G <= 0) return hipErrorInvalidDevice;
@@ -241,6 +259,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.keep_hf = (p.flags & MOE_FLAG_KEEP_H_F32) ? 1 : 0;
   P.row_done = row_done;
   P.row_done_len = row_done_len;
+  P.c_bf16 = (p.flags & MOE_FLAG_BF16_COMBINE_BUF) ? 1 : 0;
   // Anti-starvation knee (X-Stage Eq. 16): D = b_n K / (2 h) with b_n the weight
   // rows of a Linear-1 tile, K the participating workgroups and h = f, i.e.
   // the row bands one sweep of the grid covers (G / N1 here). The knee is a
@@ -262,7 +281,8 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 
   // expert waves need expert-contiguous bands; the other schedules take them largest first
   const int sort_bands = sched == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, P.N1, G, p.wave_experts, sort_bands,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, L.cap, P.N1, G, p.wave_experts,
+                     sort_bands,
                      L.Pmax,
                      P.blk_done, fp8 ? L.Pmax * (p.f / 128) : 0, reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
                      reinterpret_cast<int32_t*>(ws + L.band_rows), P.l2_full,

@@ -72,7 +72,7 @@ struct GemmParams {
   const uint8_t* W1;      // [E_l, 2f, d]
   const uint8_t* W2;      // [E_l, d, f]
   uint8_t* H;             // [cap, f] Linear-2 operand (bf16 or e4m3 codes)
-  float* C;               // combine_buf [cap, d]
+  void* C;                // combine_buf [cap, d]: fp32, or bf16 with c_bf16
   // fp8 only: block scales and the fp32 SwiGLU output before quantisation
   const float* Xs;        // [d/128, cap]  scale of X_perm row r, K block c at c*cap + r
   const float* W1s;       // [E_l, 2f/128, d/128]
@@ -100,6 +100,7 @@ struct GemmParams {
   int keep_hf;            // fp8: wide Linear-1 tiles also store their fp32 SwiGLU values in Hf
   int32_t* row_done;      // or null: per 32-row block of output rows, output elements stored (Linear-2)
   int row_done_len;       // blocks row_done holds
+  int c_bf16;             // the Linear-2 epilogue rounds its outputs to bf16 (MOE_FLAG_BF16_COMBINE_BUF)
 };
 
 // Launch the persistent expert-GEMM kernel of one operand type (bf16 in
@@ -433,11 +434,26 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
             }
           }
         } else {
+          // a destination row outside the buffer (a caller's row_dst) is not
+          // stored but reported
           const int dst = P.row_dst[t.row0 + m];
+          if ((unsigned)dst < (unsigned)P.cap) {
+            if (P.c_bf16) {
 #pragma unroll
-          for (int nb = 0; nb < G::NCB; ++nb) {
-            const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
-            P.C[(size_t)dst * P.d + col] = acc[mi][nb][i];
+              for (int nb = 0; nb < G::NCB; ++nb) {
+                const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
+                reinterpret_cast<uint16_t*>(P.C)[(size_t)dst * P.d + col] = f32_to_bf16_rne(acc[mi][nb][i]);
+              }
+            } else {
+#pragma unroll
+              for (int nb = 0; nb < G::NCB; ++nb) {
+                const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
+                reinterpret_cast<float*>(P.C)[(size_t)dst * P.d + col] = acc[mi][nb][i];
+              }
+            }
+          } else {
+            __hip_atomic_fetch_or(P.meta + META_ARG_ERR, (int)ARG_ERR_ROW_DST, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }

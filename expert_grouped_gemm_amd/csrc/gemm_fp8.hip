@@ -8,4 +8,6 @@ hipError_t launch_gemm_fp8(const GemmParams& P, int G, hipStream_t s) {
   return hipGetLastError();
 }
 
+const void* gemm_kernel_fp8() { return reinterpret_cast<const void*>(moe_gemm_kernel<true>); }
+
 }  // namespace moe

@@ -23,7 +23,11 @@ constexpr int gemm_threads(bool) { return 512; }
 constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
 constexpr int kMetaInts = 64;
-enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4 };
+enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4, META_ARG_ERR = 5 };
+// Bits of meta[META_ARG_ERR]: device-side checks of arguments the host cannot
+// see (they live in device memory). The dispatch clears its bit when it
+// starts, the expert GEMM its two.
+enum ArgErr { ARG_ERR_DISPATCH_CAP = 1, ARG_ERR_OFFSETS = 2, ARG_ERR_ROW_DST = 4 };
 
 enum GemmMode { MODE_SEP_L1 = 0, MODE_SEP_L2 = 1, MODE_WAVE = 2, MODE_INTERLEAVED = 3 };
 
@@ -60,10 +64,18 @@ inline int dispatch_chunk(int64_t Tk, int El) {
   return (int)per;
 }
 
+// Rows the workspace holds for the expert GEMM: every local assignment a
+// routing can give (T * min(k, E_l)), or more for a padded row layout.
+inline int64_t row_capacity(const moe_problem_t& p) {
+  const int El = p.e_end - p.e_begin;
+  const int64_t cap = (int64_t)p.T * (p.k < El ? p.k : El);
+  return p.row_capacity > cap ? (int64_t)p.row_capacity : cap;
+}
+
 inline Layout make_layout(const moe_problem_t& p) {
   Layout L{};
   const int El = p.e_end - p.e_begin;
-  const int64_t cap = (int64_t)p.T * (p.k < El ? p.k : El);
+  const int64_t cap = row_capacity(p);
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
   const size_t esz = fp8 ? 1 : 2;
   L.cap = (int)cap;
@@ -94,7 +106,7 @@ inline Layout make_layout(const moe_problem_t& p) {
   L.pub.x_perm_scale = take(fp8 ? cap * (p.d / 128) * 4 : 0);
   L.pub.h = take(cap * p.f * esz);
   L.pub.h_scale = take(fp8 ? cap * (p.f / 128) * 4 : 0);
-  L.pub.combine_buf = take(cap * p.d * 4);
+  L.pub.combine_buf = take(cap * p.d * ((p.flags & MOE_FLAG_BF16_COMBINE_BUF) ? 2 : 4));
   L.pub.h_f32 = take(fp8 ? cap * p.f * 4 : 0);
   // a bound on the tiles of one call: every band at the narrow widths
   // (f / 64 Linear-1 tiles and d / 128 Linear-2 tiles)
@@ -117,10 +129,10 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, co
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, float* combine_buf, hipStream_t s,
+                                 const float* W2_scale, void* combine_buf, hipStream_t s,
                                  int32_t* row_done = nullptr, int row_done_len = 0);
 
-hipError_t launch_combine(const moe_problem_t& p, const float* combine_buf, const int32_t* tok_off,
+hipError_t launch_combine(const moe_problem_t& p, const void* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
 
 // Owner-aligned return path (validated arguments; see moe_owner_plan,

@@ -98,8 +98,12 @@ __global__ __launch_bounds__(256) void segment_copy_kernel(const float* __restri
 // beside it. A segment's rows are first read after their blocks are
 // complete, rows are whole 128-byte lines (d % 128 == 0) and the launch
 // starts with the kernel-entry acquire, so neither the CU's L1 nor its XCD's
-// L2 holds a stale copy.
-__global__ __launch_bounds__(256) void segment_copy_wait_kernel(const float* __restrict__ O_pad, int R,
+// L2 holds a stale copy. O_pad is written by another kernel while this one
+// runs, so it is neither const nor restrict here, and a workgroup-scope
+// acquire fence after the poll keeps the compiler from moving a row load
+// above it (an agent-scope acquire would also invalidate the L2, which the
+// cache argument above makes unnecessary).
+__global__ __launch_bounds__(256) void segment_copy_wait_kernel(float* O_pad, int R,
                                                                 const int32_t* __restrict__ seg, int n_seg,
                                                                 int R_recv, int d,
                                                                 const int32_t* __restrict__ row_done,
@@ -131,6 +135,7 @@ __global__ __launch_bounds__(256) void segment_copy_wait_kernel(const float* __r
       }
     }
     ok = __shfl(ok, 0, 64);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (!ok) continue;
     for (int i = 0; i < n; ++i) {
       const float4* a = reinterpret_cast<const float4*>(O_pad + (size_t)(src + i) * d);
@@ -253,9 +258,11 @@ hipError_t launch_segment_copy_wait(const moe_problem_t& p, const float* O_pad, 
                                     int grid, hipStream_t s) {
   if (n_seg == 0) return hipSuccess;
   const int g = grid < n_seg ? grid : n_seg;
-  hipLaunchKernelGGL(segment_copy_wait_kernel, dim3(g), dim3(256), 0, s, O_pad, R, segs, n_seg, R_recv, p.d,
-                     row_done, err, recv);
+  hipLaunchKernelGGL(segment_copy_wait_kernel, dim3(g), dim3(256), 0, s, const_cast<float*>(O_pad), R, segs, n_seg,
+                     R_recv, p.d, row_done, err, recv);
   return hipGetLastError();
 }
+
+const void* segment_copy_wait_kernel_ptr() { return reinterpret_cast<const void*>(segment_copy_wait_kernel); }
 
 }  // namespace moe

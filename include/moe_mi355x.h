@@ -75,13 +75,13 @@ typedef enum {
 /* Tile schedule of the grouped expert GEMMs (X-Stage, Section 4.2 "MegaMoE:
  * Capacity-Aware Scheduling across Expert Waves", Algorithm 1 and Figure 4). */
 typedef enum {
-  MOE_SCHED_SEPARATE = 0,         /* one persistent launch for every Linear-1 tile, then one for every
-                                     Linear-2 tile (stream order is the only dependency) */
-  MOE_SCHED_EXPERT_WAVE = 1,      /* one persistent launch; local experts grouped into waves; a wave's
+  MOE_SCHED_EXPERT_WAVE = 0,      /* one persistent launch; local experts grouped into waves; a wave's
                                      Linear-1 tiles, then its Linear-2 tiles, then the next wave */
-  MOE_SCHED_INTERLEAVED = 2,      /* one persistent launch; Linear-1 and Linear-2 tile streams merged:
+  MOE_SCHED_INTERLEAVED = 1,      /* one persistent launch; Linear-1 and Linear-2 tile streams merged:
                                      a Linear-2 tile of row p2 is taken only when the Linear-1 cursor
                                      leads by at least lead_D rows, otherwise a Linear-1 tile */
+  MOE_SCHED_SEPARATE = 2,         /* one persistent launch for every Linear-1 tile, then one for every
+                                     Linear-2 tile (stream order is the only dependency) */
   MOE_SCHED_AUTO = 3              /* chosen at run time (X-Stage, Section 6.3: pick the schedule per
                                      routing and working set). The expert-wave and interleaved orders
                                      exist to spread remote-store bursts; this library's epilogues
@@ -90,28 +90,36 @@ typedef enum {
                                      counters (measured fastest on every workload shape here) */
 } moe_sched_t;
 
-/* Tile-shape controls of the grouped expert GEMMs. Every combination gives
- * bit-identical results (each output element is computed by one tile with the
- * same K order); they exist for tests and tuning. By default the widths and
- * the raster order are chosen from the shape. */
+/* Flags (moe_problem_t.flags). Bits 0 and 1 select output and buffer
+ * precisions; the tile-shape controls (bits 2-4) give bit-identical results
+ * whatever their combination (each output element is computed by one tile
+ * with the same K order) and exist for tests and tuning: by default the
+ * widths and the raster order are chosen from the shape. */
 enum {
   MOE_FLAG_NONE = 0u,
-  MOE_FLAG_TILE_NARROW = 1u,      /* every tile 128 weight rows wide */
-  MOE_FLAG_TILE_WIDE = 2u,        /* 256 weight rows wide wherever the shape allows (Linear-2 tiles need
-                                     d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
-  MOE_FLAG_BAND_MAJOR = 4u,       /* walk the expert-GEMM tile lists row band by row band instead of
-                                     in groups of bands */
-  MOE_FLAG_TILE_TRACE = 8u,       /* record one span per expert-GEMM tile in the workspace region
-                                     tile_trace (moe_tile_record_t); costs a few clock reads per tile */
-  MOE_FLAG_KEEP_H_F32 = 16u,      /* fp8: also store every fp32 SwiGLU value (the H quantiser's input)
-                                     in the workspace region h_f32. Without it, wide Linear-1 tiles
-                                     quantise from on-chip memory and leave h_f32 unwritten. For
-                                     verification; costs 4 bytes of HBM writes per H element */
-  MOE_FLAG_TEST_WAIT_TIMEOUT = 32u /* tests of the timeout path only: the fused schedules' readiness
-                                     target is made unreachable, so their first Linear-2 wait gives up
-                                     after its bounded spin (about a second), every later wait at once,
-                                     and moe_check_workspace reports MOE_ERR_DEADLOCK. Outputs are
-                                     then invalid. The separate schedule has no such wait */
+  MOE_FLAG_FP32_Y_DEBUG = 1u << 0,     /* moe_layer_forward also returns the fp32 sums of Y before their
+                                          bf16 rounding in Y_fp32. A non-NULL Y_fp32 alone requests them
+                                          too; with the flag set Y_fp32 must not be NULL */
+  MOE_FLAG_BF16_COMBINE_BUF = 1u << 1, /* the token-ordered combine buffer holds bf16 instead of fp32: the
+                                          Linear-2 epilogue rounds each expert output to bf16 (RNE) and the
+                                          combine reads bf16. Halves the buffer's bytes, at the price of a
+                                          second rounding of every output (measured, not the default) */
+  MOE_FLAG_TILE_NARROW = 1u << 2,      /* every tile 128 weight rows wide */
+  MOE_FLAG_TILE_WIDE = 1u << 3,        /* 256 weight rows wide wherever the shape allows (Linear-2 tiles
+                                          need d % 256 == 0); may not be combined with MOE_FLAG_TILE_NARROW */
+  MOE_FLAG_BAND_MAJOR = 1u << 4,       /* walk the expert-GEMM tile lists row band by row band instead of
+                                          in groups of bands */
+  MOE_FLAG_TILE_TRACE = 1u << 5,       /* record one span per expert-GEMM tile in the workspace region
+                                          tile_trace (moe_tile_record_t); costs a few clock reads per tile */
+  MOE_FLAG_KEEP_H_F32 = 1u << 6,       /* fp8: also store every fp32 SwiGLU value (the H quantiser's input)
+                                          in the workspace region h_f32. Without it, wide Linear-1 tiles
+                                          quantise from on-chip memory and leave h_f32 unwritten. For
+                                          verification; costs 4 bytes of HBM writes per H element */
+  MOE_FLAG_TEST_WAIT_TIMEOUT = 1u << 7 /* tests of the timeout path only: the fused schedules' readiness
+                                          target is made unreachable, so their first Linear-2 wait gives up
+                                          after its bounded spin (about a second), every later wait at once,
+                                          and moe_check_workspace reports MOE_ERR_DEADLOCK. Outputs are
+                                          then invalid. The separate schedule has no such wait */
 };
 
 /* One expert-GEMM tile as recorded with MOE_FLAG_TILE_TRACE: the per-tile
@@ -151,10 +159,15 @@ typedef struct moe_problem {
                             tiles fill the persistent grid */
   int32_t grid;          /* persistent workgroups; 0 = one per compute unit */
   uint32_t flags;        /* MOE_FLAG_* bits; 0 = tile shapes chosen from the problem's shape */
+  int32_t row_capacity;  /* rows the workspace holds for the expert GEMM: 0 = T * min(k, E_l), the most
+                            local assignments a routing can give; larger (>= that) for a padded row
+                            layout such as the owner-aligned one below, whose R can exceed it */
 } moe_problem_t;
 
 /* Byte offsets of the intermediates inside a workspace (for inspection by
- * tests and callers; moe_layer_forward writes all of them). cap = T * min(k, E_l). */
+ * tests and callers). cap = the row capacity: T * min(k, E_l), or
+ * p->row_capacity if set. moe_layer_forward writes every region except one
+ * whose output the caller passes in its place. */
 typedef struct moe_workspace_layout {
   size_t topk_idx;      /* int32 [T, k]                                     */
   size_t topk_w;        /* fp32  [T, k]                                     */
@@ -171,8 +184,12 @@ typedef struct moe_workspace_layout {
   size_t h_f32;         /* fp32  [cap, f]   fp8 only: SwiGLU output before its e4m3 quantisation */
   size_t combine_buf;   /* fp32  [cap, d]   Linear-2 output in token-order slots */
   size_t meta;          /* int32 [64]       meta[0] = A (local assignments), meta[1] = row bands,
-                                            meta[2] = error flag of the last call (1 = wait timed out),
-                                            meta[4] = tile records written (MOE_FLAG_TILE_TRACE) */
+                                            meta[2] = 1 if a readiness wait of the last expert-GEMM
+                                            call timed out, meta[4] = tile records written
+                                            (MOE_FLAG_TILE_TRACE), meta[5] = device-side argument
+                                            errors (bits: 1 = more local assignments than the row
+                                            capacity, 2 = offsets not monotone or past the row
+                                            capacity, 4 = a row_dst outside the row capacity) */
   size_t tile_trace;    /* moe_tile_record_t [tile_trace_capacity]; empty without MOE_FLAG_TILE_TRACE */
   size_t tile_trace_capacity;  /* records (a bound on the tiles of one call) */
   size_t total;         /* = moe_workspace_size */
@@ -208,31 +225,55 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
 /* Grouped expert FFN over the expert-contiguous rows (X-Stage Section 2.2;
  * schedule per p->sched). W1 [E_l, 2f, d], W2 [E_l, d, f] (bf16, or e4m3 codes
  * with W1_scale fp32 [E_l, 2f/128, d/128], W2_scale fp32 [E_l, d/128, f/128]).
- * Writes combine_buf fp32 [cap, d]: row row_dst[r] = W2[e] act(r). The
- * intermediate H lives in the workspace. offsets/row_dst as from moe_dispatch. */
+ * Writes combine_buf [cap, d] (fp32, or bf16 with MOE_FLAG_BF16_COMBINE_BUF):
+ * row row_dst[r] = W2[e] act(r). The intermediate H lives in the workspace.
+ * offsets/row_dst as from moe_dispatch. Device-side checks (reported by
+ * moe_check_workspace as MOE_ERR_INVALID_ARGUMENT): offsets must be
+ * non-decreasing with 0 <= offsets[0] and offsets[E_l] <= cap, otherwise no
+ * tile runs and combine_buf and H are left untouched; a row whose row_dst lies
+ * outside [0, cap) is not stored. */
 MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
                                         const int32_t* offsets, const int32_t* row_dst, const void* W1,
                                         const float* W1_scale, const void* W2, const float* W2_scale,
-                                        float* combine_buf, void* workspace, size_t ws_bytes, void* stream);
+                                        void* combine_buf, void* workspace, size_t ws_bytes, void* stream);
 
 /* Weighted combine (Cui et al. Section 2.1 step (5)): Y bf16 [T, d] in
  * output-row order q; Y_fp32 [T, d] (may be NULL) gets the same sums before
- * the bf16 rounding. Deterministic: fixed slot order, no atomics. */
-MOE_API moe_status_t moe_combine(const moe_problem_t* p, const float* combine_buf, const int32_t* tok_off,
+ * the bf16 rounding. combine_buf [cap, d] is fp32, or bf16 with
+ * MOE_FLAG_BF16_COMBINE_BUF. Deterministic: fixed slot order, no atomics. A
+ * row q whose slot range [tok_off[q], tok_off[q+1]) does not lie inside
+ * [0, cap) is written as NaN (a device-side check; nothing outside the
+ * buffers is read). */
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf, const int32_t* tok_off,
                                  const float* comb_w, void* Y, float* Y_fp32, void* stream);
 
-/* The whole share: route -> dispatch -> experts -> combine on one stream,
- * with row counts kept on the device (no host synchronisation). Every
- * intermediate is left in the workspace at moe_workspace_get_layout's offsets. */
+/* The whole share, Cui et al. Section 2.1 steps (1)-(5) as one GPU's local
+ * pipeline (dispatch and return become on-GPU permutations) and X-Stage
+ * Section 2.2 "MegaMoE Execution" (Dispatch, Linear-1, activation, Linear-2,
+ * Combine): route -> dispatch -> grouped Linear-1 + SwiGLU -> grouped
+ * Linear-2 -> combine on one stream, with row counts kept on the device (no
+ * host synchronisation). Inputs as for the component calls; Y bf16 [T, d]
+ * (segment-major with S > 1); Y_fp32 [T, d] or NULL (see
+ * MOE_FLAG_FP32_Y_DEBUG). The optional outputs, each DEVICE memory or NULL,
+ * receive the routing and dispatch results: topk_idx_out int32 [T, k],
+ * topk_w_out fp32 [T, k], counts_out int32 [E_l], offsets_out int32
+ * [E_l + 1], row_src_out int32 [cap] (rows >= A untouched). A non-NULL output
+ * is written in place of its workspace region, which the call then leaves
+ * unwritten. Every other intermediate is left in the workspace at
+ * moe_workspace_get_layout's offsets. */
 MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
                                        const float* logits, const void* W1, const float* W1_scale,
                                        const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
-                                       void* workspace, size_t ws_bytes, void* stream);
+                                       void* workspace, size_t ws_bytes, int32_t* topk_idx_out,
+                                       float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                       int32_t* row_src_out, void* stream);
 
-/* Synchronises `stream` and reads the workspace's error flag, which every
- * moe_expert_forward / moe_layer_forward call clears when it starts:
- * MOE_ERR_DEADLOCK if a persistent-pipeline wait of the most recent call on
- * this workspace timed out (its outputs are then invalid). Clears the flag. */
+/* Synchronises `stream` and reads the workspace's error words (meta[2],
+ * meta[5]), which the calls that can set them clear when they start:
+ * MOE_ERR_DEADLOCK if a persistent-pipeline wait of the most recent
+ * expert-GEMM call on this workspace timed out, MOE_ERR_INVALID_ARGUMENT if a
+ * device-side check of the last dispatch or expert-GEMM call failed (its
+ * outputs are then invalid). Clears both words. */
 MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace, size_t ws_bytes,
                                          void* stream);
 
@@ -281,12 +322,13 @@ MOE_API moe_status_t moe_owner_plan(const moe_problem_t* p, const int32_t* topk_
  * e4m3 codes with X_scale fp32 [T/128, d/128]; X_scale must be NULL for
  * bf16), row_src int32 [R] from moe_owner_plan. X_pad [R, d] out: row r =
  * X[row_src[r] / k], or zeros where row_src[r] is -1 (ids outside [0, T*k)
- * also give zeros). fp8: X_pad_scale fp32 [d/128, cap] out, cap = T *
- * min(k, E_l): row r's block scales at c * cap + r (the layout
- * moe_expert_forward reads; 1 for a zero row); R > cap gives
- * MOE_ERR_UNSUPPORTED. moe_expert_forward then runs on X_pad with offsets =
- * expert_off and row_dst[r] = r, writing the layout's expert outputs O_pad
- * fp32 [R, d] (requires R <= cap, the workspace's row capacity). */
+ * also give zeros). fp8: X_pad_scale fp32 [d/128, cap] out, cap = the row
+ * capacity of p (T * min(k, E_l), or p->row_capacity): row r's block scales
+ * at c * cap + r (the layout moe_expert_forward reads; 1 for a zero row);
+ * R > cap gives MOE_ERR_UNSUPPORTED. moe_expert_forward then runs on X_pad
+ * with offsets = expert_off and row_dst[r] = r, writing the layout's expert
+ * outputs O_pad fp32 [R, d]; this needs R <= cap, so a padded layout sets
+ * p->row_capacity to at least R (moe_owner_plan reports R). */
 MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, const float* X_scale,
                                       const int32_t* row_src, int64_t R, void* X_pad, float* X_pad_scale,
                                       void* stream);
@@ -310,19 +352,25 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
  * row_done_len are dropped.
  *
  * moe_segment_copy_wait: moe_segment_copy whose segments each wait until
- * their rows' blocks are complete in row_done (ceil(R / 32) <= row_done_len),
+ * their rows' blocks are complete in row_done (ceil(R / 32) <= row_done_len).
+ * R is the layout's row count, expert_off[E_l] of the plan: the GEMM stores
+ * exactly those rows, so the last block's target is taken from it (O_pad
+ * must hold at least R rows, and may hold more),
  * so it can run on a second stream beside moe_expert_forward_signal (launch
  * it after the clearing of row_done is ordered before it). grid persistent
  * workgroups (1..1024; 0 = 256, one per compute unit) walk the segments in plan order; they use no
  * LDS, so the GEMM's workgroups stay resident beside them. Waits are
  * bounded: a timeout (about a second) sets *err (DEVICE int32, zero at the
- * call) to 1, and that and every later segment are skipped. fp8 problems
- * give MOE_ERR_UNSUPPORTED: the fp8 GEMM's wavefronts take a SIMD's whole
- * register file, so no copier wavefront can run beside its workgroups. */
+ * call) to 1, and that and every later segment are skipped. The call gives
+ * MOE_ERR_UNSUPPORTED when the register counts the runtime reports for the
+ * problem's expert-GEMM kernel (two wavefronts per SIMD) and for the copier
+ * do not fit one SIMD's 512 registers per lane together: then no copier
+ * wavefront could run beside the GEMM's workgroups and every wait would time
+ * out (the fp8 GEMM, at 256 registers per wavefront, is such a case). */
 MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
                                                const float* X_perm_scale, const int32_t* offsets,
                                                const int32_t* row_dst, const void* W1, const float* W1_scale,
-                                               const void* W2, const float* W2_scale, float* combine_buf,
+                                               const void* W2, const float* W2_scale, void* combine_buf,
                                                int32_t* row_done, int64_t row_done_len, void* workspace,
                                                size_t ws_bytes, void* stream);
 MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* O_pad, int64_t R,

@@ -44,7 +44,7 @@ def test_version_and_status_strings(L):
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(moe.Problem) == 15 * 4
+    assert ctypes.sizeof(moe.Problem) == 16 * 4
     assert ctypes.sizeof(moe.WorkspaceLayout) == 18 * 8
 
 
@@ -66,7 +66,8 @@ def test_unsupported_shapes(L, over, code):
 
 
 def test_invalid_enums_and_flags(L):
-    for field, val in (("dtype", 7), ("sched", 4), ("flags", 3), ("flags", 64), ("lead_D", -1), ("grid", -2)):
+    for field, val in (("dtype", 7), ("sched", 4), ("sched", -1), ("flags", 12), ("flags", 256), ("lead_D", -1),
+                       ("grid", -2), ("row_capacity", -1)):
         p = moe.make_problem(**GOOD)
         setattr(p, field, val)
         out = moe.WorkspaceLayout()
@@ -92,22 +93,49 @@ def test_null_and_small_workspace_rejected_before_launch(L):
     p = moe.make_problem(**GOOD)
     need = L.moe_workspace_size(ctypes.byref(p))
     fake = ctypes.c_void_p(1 << 20)           # never dereferenced: validation fails first
+    none5 = [None] * 5                        # the optional routing / dispatch outputs
+
+    def layer(*a, outs=none5):
+        return L.moe_layer_forward(ctypes.byref(p), *a, *outs, None)
     # X NULL; then X_scale given for bf16 (inconsistent)
-    assert L.moe_layer_forward(ctypes.byref(p), None, None, fake, fake, None, fake, None, fake, None, fake,
-                               ctypes.c_size_t(need), None) == 1
-    assert L.moe_layer_forward(ctypes.byref(p), fake, fake, *([fake] * 8), ctypes.c_size_t(need), None) == 1
+    assert layer(None, None, fake, fake, None, fake, None, fake, None, fake, ctypes.c_size_t(need)) == 1
+    assert layer(fake, fake, *([fake] * 8), ctypes.c_size_t(need)) == 1
     # bf16 with a non-NULL W1 scale pointer is inconsistent
-    assert L.moe_layer_forward(ctypes.byref(p), fake, None, fake, fake, fake, fake, None, fake, None, fake,
-                               ctypes.c_size_t(need), None) == 1
+    assert layer(fake, None, fake, fake, fake, fake, None, fake, None, fake, ctypes.c_size_t(need)) == 1
     # workspace smaller than required
-    assert L.moe_layer_forward(ctypes.byref(p), fake, None, fake, fake, None, fake, None, fake, None, fake,
-                               ctypes.c_size_t(need - 1), None) == 3
-    # misaligned workspace / tensors
-    assert L.moe_layer_forward(ctypes.byref(p), fake, None, fake, fake, None, fake, None, fake, None,
-                               ctypes.c_void_p((1 << 20) + 16), ctypes.c_size_t(need), None) == 1
+    assert layer(fake, None, fake, fake, None, fake, None, fake, None, fake, ctypes.c_size_t(need - 1)) == 3
+    # misaligned workspace / tensors / optional outputs
+    assert layer(fake, None, fake, fake, None, fake, None, fake, None, ctypes.c_void_p((1 << 20) + 16),
+                 ctypes.c_size_t(need)) == 1
+    assert layer(fake, None, fake, fake, None, fake, None, fake, None, fake, ctypes.c_size_t(need),
+                 outs=[None, None, ctypes.c_void_p((1 << 20) + 2), None, None]) == 1
+    # MOE_FLAG_FP32_Y_DEBUG without a Y_fp32 buffer
+    p.flags = moe.FLAG_FP32_Y_DEBUG
+    assert layer(fake, None, fake, fake, None, fake, None, fake, None, fake, ctypes.c_size_t(need)) == 1
+    p.flags = 0
     assert L.moe_combine(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 4), fake, fake, fake, None, None) == 1
     assert L.moe_route_topk(ctypes.byref(p), None, fake, fake, None, None) == 1
     assert L.moe_route_topk(None, fake, fake, fake, None, None) == 1
+
+
+def test_row_capacity_sizes_the_workspace(L):
+    """row_capacity raises the rows the GEMM regions hold (a padded layout),
+    never lowers them below T * min(k, E_l)."""
+    base = moe.make_problem(T=256, d=128, f=256, E_global=8, k=2, e_begin=0, e_end=4)
+    small = moe.make_problem(T=256, d=128, f=256, E_global=8, k=2, e_begin=0, e_end=4, row_capacity=100)
+    big = moe.make_problem(T=256, d=128, f=256, E_global=8, k=2, e_begin=0, e_end=4, row_capacity=2000)
+    assert moe.workspace_size(small) == moe.workspace_size(base)
+    lb, lg = moe.workspace_layout(base), moe.workspace_layout(big)
+    assert moe.row_capacity(big) == 2000 and moe.row_capacity(base) == 512
+    assert lg.combine_buf - lg.h >= 2000 * 256 * 2
+    assert lg.total - lb.total >= (2000 - 512) * (128 * 2 + 256 * 2 + 128 * 4)
+
+
+def test_bf16_combine_buffer_halves_its_region(L):
+    p32 = moe.make_problem(**GOOD)
+    p16 = moe.make_problem(**GOOD, bf16_combine_buf=True)
+    cap = 64 * 2
+    assert moe.workspace_size(p32) - moe.workspace_size(p16) >= cap * 128 * 2 - 256
 
 
 def test_binding_rejects_cpu_tensors():

@@ -22,11 +22,18 @@ from oracle import owner_layout as ol
 pytestmark = pytest.mark.gpu
 
 
+def padded_problem(p, R):
+    """p with a workspace row capacity that holds the R padded rows."""
+    q = moe.Problem.from_buffer_copy(p)
+    q.row_capacity = max(R, moe.row_capacity(p))
+    return q
+
+
 def _owner_return(p, g, idx, local, tb, x):
     plan = moe.owner_plan(p, idx, local, tb, x)
-    R, El = plan["R"], p.e_end - p.e_begin
-    cap = p.T * min(p.k, El)
-    assert R <= cap, f"padded rows {R} exceed the workspace row capacity {cap}"
+    R = plan["R"]
+    p = padded_problem(p, R)
+    cap = moe.row_capacity(p)
     row_src = torch.from_numpy(plan["row_src"]).cuda()
     fp8 = p.dtype == moe.DTYPE["fp8_e4m3"]
     X_pad = torch.empty((R, p.d), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
@@ -62,6 +69,10 @@ SMALL = {
                                         num_segments=8, seed=22), 0, 16, 3),
     "zipf_s2": (moe_synth.make_config("tiny", T=2048, d=256, f=256, E_global=16, k=4, e_begin=0, e_end=8,
                                       zipf_s=1.2, num_segments=2, seed=23), 1, 64, 2),
+    # every expert local: any padding takes the layout past T * min(k, E_l),
+    # so the workspace is sized by row_capacity
+    "all_local_s4": (moe_synth.make_config("tiny", T=512, d=256, f=256, E_global=8, k=2, e_begin=0, e_end=8,
+                                           num_segments=4, seed=26), 1, 32, 2),
 }
 
 
@@ -77,6 +88,8 @@ def test_owner_return_small(name):
     fused, idx = _fused_outputs_by_assignment(p, ws)
     np.testing.assert_array_equal(idx, ref["topk_idx"])
     plan, X_pad, recv = _owner_return(p, g, idx, local, tb, x)
+    if name == "all_local_s4":
+        assert plan["R"] > cfg.cap
     # padded gather: X rows bit-exact, zero rows where row_src = -1
     rs = plan["row_src"]
     xs = inp["X"].view(torch.int16).numpy()
@@ -125,6 +138,7 @@ def _overlapped(p, X, g, plan, ws, grid=0):
     """Gather, then the signalling GEMM on the launch stream and the waiting
     segment copier on a second stream (default priority), started together."""
     R = plan["R"]
+    p = padded_problem(p, R)
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     row_src = torch.from_numpy(plan["row_src"]).cuda()
@@ -140,7 +154,7 @@ def _overlapped(p, X, g, plan, ws, grid=0):
     ev = torch.cuda.Event()
     ev.record(main)
     side.wait_event(ev)
-    moe.segment_copy_wait(p, O_pad, segs, recv, row_done, err, grid, stream=side)
+    moe.segment_copy_wait(p, O_pad, R, segs, recv, row_done, err, grid, stream=side)
     moe.expert_forward_signal(p, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad, row_done, ws,
                               stream=main)
     main.wait_stream(side)
@@ -148,7 +162,7 @@ def _overlapped(p, X, g, plan, ws, grid=0):
     return recv, int(err.item()), row_done
 
 
-@pytest.mark.parametrize("name", ["share_s4", "ragged_s8"])
+@pytest.mark.parametrize("name", ["share_s4", "ragged_s8", "all_local_s4"])
 def test_overlapped_copy_matches_stream_ordered(name):
     cfg, local, tb, x = SMALL[name]
     print(f"overlapped owner return {name}", flush=True)
@@ -158,7 +172,7 @@ def test_overlapped_copy_matches_stream_ordered(name):
     _, _, ws = run_layer(p, g)
     idx = moe.workspace_views(p, ws)["topk_idx"].cpu().numpy()
     plan = moe.owner_plan(p, idx, local, tb, x)
-    ws2 = moe.alloc_workspace(p)
+    ws2 = moe.alloc_workspace(padded_problem(p, plan["R"]))
     # two calls in a row, the second on other token values (no stale rows may be copied)
     X2 = moe_synth.generate(cfg, seed=cfg.seed + 100)["X"].cuda()
     for X in (g["X"], X2):
@@ -180,7 +194,7 @@ def test_overlapped_copy_deepseek_share_full_size():
     _, _, ws = run_layer(p, g)
     idx = moe.workspace_views(p, ws)["topk_idx"].cpu().numpy()
     plan, _, want = _owner_return(p, g, idx, 0, 32, 2)
-    recv, err, _ = _overlapped(p, g["X"], g, plan, moe.alloc_workspace(p))
+    recv, err, _ = _overlapped(p, g["X"], g, plan, moe.alloc_workspace(padded_problem(p, plan["R"])))
     assert err == 0
     torch.testing.assert_close(recv, want, rtol=0, atol=0)
 
@@ -200,7 +214,7 @@ def test_copier_wait_timeout_is_reported():
     row_done = torch.zeros((R + 31) // 32, dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     segs = torch.from_numpy(plan["segments"]).cuda().contiguous()
-    moe.segment_copy_wait(p, O_pad, segs, recv, row_done, err, grid=4)
+    moe.segment_copy_wait(p, O_pad, R, segs, recv, row_done, err, grid=4)
     torch.cuda.synchronize()
     assert int(err.item()) == 1
     assert torch.isnan(recv).all()
@@ -219,7 +233,7 @@ def test_owner_return_fp8():
     fused, idx = _fused_outputs_by_assignment(p, ws)
     plan = moe.owner_plan(p, idx, 2, 32, 2)
     R, cap = plan["R"], cfg.cap
-    assert R <= cap
+    assert R <= cap  # the gather's scale rows are laid out with the problem's row capacity
     row_src = torch.from_numpy(plan["row_src"]).cuda()
     X_pad = torch.empty((R, p.d), dtype=torch.uint8, device="cuda")
     X_pad_scale = torch.full((p.d // 128, cap), -7.0, dtype=torch.float32, device="cuda")

@@ -437,9 +437,10 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         row_done.zero_()
         ev.record(stream)
         side.wait_event(ev)
-        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
+        # the GEMM first: on a shared hardware queue the copier then follows it
         moe.expert_forward_signal(p8b, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
                                   g.get("W2_scale"), O_pad, row_done, ws8, stream)
+        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
         stream.wait_stream(side)
 
     def overlapped_raster():
@@ -447,9 +448,9 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
         row_done.zero_()
         ev.record(stream)
         side.wait_event(ev)
-        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
         moe.expert_forward_signal(p8, X_pad, X_pad_scale, eo, iota, g["W1"], g.get("W1_scale"), g["W2"],
                                   g.get("W2_scale"), O_pad, row_done, ws8, stream)
+        moe.segment_copy_wait(p8, O_pad, R, segs, recv, row_done, err, 0, side)
         stream.wait_stream(side)
 
     def sequential():

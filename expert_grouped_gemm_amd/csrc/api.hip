@@ -108,7 +108,8 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
   if (!aligned16(X) || !aligned16(X_perm)) return MOE_ERR_INVALID_ARGUMENT;
   moe::Layout L = moe::make_layout(*p);
   if ((st = check_ws(L, workspace, ws_bytes)) != MOE_OK) return st;
-  hipError_t e = moe::launch_dispatch(*p, L, static_cast<char*>(workspace), X, X_scale, topk_idx, topk_w, counts,
+  hipError_t e = moe::launch_dispatch(*p, L, moe::dispatch_scratch(L, static_cast<char*>(workspace)), X, X_scale,
+                                      topk_idx, topk_w, counts,
                                       offsets, row_src, row_dst, tok_off, comb_w, X_perm, X_perm_scale,
                                       (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
@@ -177,11 +178,13 @@ MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, co
   int32_t* row_src = row_src_out ? row_src_out : I(W.row_src);
   hipError_t e = moe::launch_route(*p, logits, idx, wts, nullptr, s);
   if (e == hipSuccess)
-    e = moe::launch_dispatch(*p, L, ws, X, X_scale, idx, wts, counts, offsets, row_src, I(W.row_dst), I(W.tok_off),
+    e = moe::launch_dispatch(*p, L, moe::dispatch_scratch(L, ws), X, X_scale, idx, wts, counts, offsets, row_src,
+                             I(W.row_dst), I(W.tok_off),
                              F(W.comb_w), ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, s);
   if (e == hipSuccess)
     e = moe::launch_expert_forward(*p, L, ws, ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, offsets,
-                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, ws + W.combine_buf, s);
+                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, ws + W.combine_buf, s, nullptr, 0,
+                                   true);
   if (e == hipSuccess) e = moe::launch_combine(*p, ws + W.combine_buf, I(W.tok_off), F(W.comb_w), Y, Y_fp32, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
@@ -198,7 +201,7 @@ MOE_API moe_status_t moe_check_workspace(const moe_problem_t* p, void* workspace
   hipError_t e = hipMemcpyAsync(host, meta, sizeof(host), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
-  const bool timed_out = host[moe::META_ERR] != 0, bad_arg = host[moe::META_ARG_ERR] != 0;
+  const bool timed_out = host[moe::META_ERR] != 0, bad_arg = (host[moe::META_ARG_ERR] & moe::ARG_ERR_ALL) != 0;
   if (timed_out || bad_arg) {
     const int32_t zero = 0;
     e = hipMemcpyAsync(meta + moe::META_ERR, &zero, sizeof(zero), hipMemcpyHostToDevice, s);

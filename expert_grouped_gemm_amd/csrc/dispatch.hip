@@ -31,9 +31,10 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
                                                              int32_t* __restrict__ tok_cnt,
                                                              int32_t* __restrict__ meta) {
   const int Tk = T * k;
-  if (blockIdx.x == 0 && threadIdx.x == 0)  // this call's capacity check starts clear
-    __hip_atomic_fetch_and(meta + META_ARG_ERR, ~(int)ARG_ERR_DISPATCH_CAP, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // the error words report this call only
+    meta[META_ERR] = 0;
+    meta[META_ARG_ERR] = 0;
+  }
   extern __shared__ int32_t hist_all[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x * 4 + w;
@@ -288,14 +289,14 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const uint8_t* __r
 
 }  // namespace
 
-hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, const void* X,
+hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, const DispatchScratch& sc, const void* X,
                            const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,
                            int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
                            float* comb_w, void* X_perm, float* X_perm_scale, hipStream_t s) {
   const int El = L.E_l;
-  int32_t* blk = reinterpret_cast<int32_t*>(ws + L.blk_counts);
-  int32_t* meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
-  int32_t* tok_cnt = reinterpret_cast<int32_t*>(ws + L.tok_cnt);
+  int32_t* blk = sc.blk_counts;
+  int32_t* meta = sc.meta;
+  int32_t* tok_cnt = sc.tok_cnt;
   hipLaunchKernelGGL(dispatch_count_kernel, dim3((L.nblk + 3) / 4), dim3(256), 4 * El * 4, s, idx, p.T, p.k,
                      p.num_segments, L.chunk, p.e_begin, El, L.nblk, blk, tok_cnt, meta);
   hipError_t e = hipGetLastError();

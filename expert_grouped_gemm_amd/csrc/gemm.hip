@@ -16,6 +16,7 @@ namespace {
 // stored, and the error bit is set for moe_check_workspace.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int El, int cap, int N1,
                                                     int G, int wave_experts, int sort_bands, int Pmax,
+                                                    int clear_bits,
                                                     int32_t* __restrict__ blk_done,
                                                     int nblk_done, int32_t* __restrict__ band_expert,
                                                     int32_t* __restrict__ band_row0,
@@ -28,8 +29,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (threadIdx.x == 0) {
     meta[META_ERR] = 0;  // the flag reports this call only
     meta[META_TRACE_N] = 0;
-    __hip_atomic_fetch_and(meta + META_ARG_ERR, ~(int)(ARG_ERR_OFFSETS | ARG_ERR_ROW_DST), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_and(meta + META_ARG_ERR, ~clear_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int e = threadIdx.x;
   int cnt = 0, nb = 0;
@@ -219,7 +219,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
                                  const float* W2_scale, void* combine_buf, hipStream_t s, int32_t* row_done,
-                                 int row_done_len) {
+                                 int row_done_len, bool after_dispatch) {
   const int G = gemm_grid(p);
   if (G <= 0) return hipErrorInvalidDevice;
   const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
@@ -281,9 +281,11 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 
   // expert waves need expert-contiguous bands; the other schedules take them largest first
   const int sort_bands = sched == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
+  // a standalone call clears every error bit; after the dispatch of the same
+  // call, only the GEMM's own
+  const int clear_bits = after_dispatch ? (ARG_ERR_OFFSETS | ARG_ERR_ROW_DST) : ARG_ERR_ALL;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L.E_l, L.cap, P.N1, G, p.wave_experts,
-                     sort_bands,
-                     L.Pmax,
+                     sort_bands, L.Pmax, clear_bits,
                      P.blk_done, fp8 ? L.Pmax * (p.f / 128) : 0, reinterpret_cast<int32_t*>(ws + L.band_expert), reinterpret_cast<int32_t*>(ws + L.band_row0),
                      reinterpret_cast<int32_t*>(ws + L.band_rows), P.l2_full,
                      reinterpret_cast<int32_t*>(ws + L.wave_band0), P.meta);

@@ -25,9 +25,11 @@ constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent w
 constexpr int kMetaInts = 64;
 enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4, META_ARG_ERR = 5 };
 // Bits of meta[META_ARG_ERR]: device-side checks of arguments the host cannot
-// see (they live in device memory). The dispatch clears its bit when it
-// starts, the expert GEMM its two.
-enum ArgErr { ARG_ERR_DISPATCH_CAP = 1, ARG_ERR_OFFSETS = 2, ARG_ERR_ROW_DST = 4 };
+// see (they live in device memory). A call that uses a workspace clears the
+// whole word when it starts (the workspace may hold anything before its first
+// use); inside moe_layer_forward the expert GEMM clears only its own bits, so
+// the dispatch's report survives until moe_check_workspace reads it.
+enum ArgErr { ARG_ERR_DISPATCH_CAP = 1, ARG_ERR_OFFSETS = 2, ARG_ERR_ROW_DST = 4, ARG_ERR_ALL = 7 };
 
 enum GemmMode { MODE_SEP_L1 = 0, MODE_SEP_L2 = 1, MODE_WAVE = 2, MODE_INTERLEAVED = 3 };
 
@@ -121,7 +123,19 @@ inline Layout make_layout(const moe_problem_t& p) {
 hipError_t launch_route(const moe_problem_t& p, const float* logits, int32_t* idx, float* w,
                         int32_t* counts_global, hipStream_t s);
 
-hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, char* ws, const void* X,
+// The dispatch's own scratch: per-(expert, chunk) counts [E_l, nblk], local
+// slots per output row [T], and the meta words (A, error bits).
+struct DispatchScratch {
+  int32_t* blk_counts;
+  int32_t* tok_cnt;
+  int32_t* meta;
+};
+inline DispatchScratch dispatch_scratch(const Layout& L, char* ws) {
+  return {reinterpret_cast<int32_t*>(ws + L.blk_counts), reinterpret_cast<int32_t*>(ws + L.tok_cnt),
+          reinterpret_cast<int32_t*>(ws + L.pub.meta)};
+}
+
+hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, const DispatchScratch& sc, const void* X,
                            const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,
                            int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
                            float* comb_w, void* X_perm, float* X_perm_scale, hipStream_t s);
@@ -130,7 +144,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
                                  const void* W1, const float* W1_scale, const void* W2,
                                  const float* W2_scale, void* combine_buf, hipStream_t s,
-                                 int32_t* row_done = nullptr, int row_done_len = 0);
+                                 int32_t* row_done = nullptr, int row_done_len = 0, bool after_dispatch = false);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);

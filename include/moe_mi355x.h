@@ -357,7 +357,11 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
  * exactly those rows, so the last block's target is taken from it (O_pad
  * must hold at least R rows, and may hold more),
  * so it can run on a second stream beside moe_expert_forward_signal (launch
- * it after the clearing of row_done is ordered before it). grid persistent
+ * it after the clearing of row_done is ordered before it). Enqueue the
+ * GEMM first and the copier second: two streams may share one hardware
+ * queue, and a copier enqueued first on a shared queue would hold the GEMM
+ * back until its waits time out; in the other order the worst case is that
+ * the copier runs after the GEMM. grid persistent
  * workgroups (1..1024; 0 = 256, one per compute unit) walk the segments in plan order; they use no
  * LDS, so the GEMM's workgroups stay resident beside them. Waits are
  * bounded: a timeout (about a second) sets *err (DEVICE int32, zero at the

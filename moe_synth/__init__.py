@@ -16,6 +16,9 @@ Overlooked Pipeline Stage ...", Section 2.2):
   mixtral              T=16384, d=4096, f=14336, E=8,   k=2
   deepseek_share_fp8   as deepseek_share_bf16, e4m3 + 128x128 fp32 block
                        scales, 8 destination segments (token t -> t mod 8)
+  deepseek_share_w4a8  as deepseek_share_fp8, but W1 and W2 in MXFP4 (E2M1
+                       elements, one E8M0 scale per 32 along K): the low-bit
+                       weight variant the X-Stage evaluation runs beside W8A8
 
 Draw order (one torch.Generator per call, seeded): X, then logits, then W1
 expert by expert, then W2 expert by expert. All draws are fp32 standard
@@ -29,6 +32,14 @@ Storage formats produced here:
   e4m3   : torch.uint8 bit patterns of OCP E4M3FN values plus fp32 block scales
            scale = amax(block) / 448 (1 if the block is all zero); code =
            torch's fp32 -> float8_e4m3fn cast of clamp(x / scale, -448, 448).
+  mxfp4  : weights only. Per row, per 32 consecutive elements along K, the
+           OCP MX conversion: shared exponent = floor(log2(amax)) - 2 (2 is
+           the largest E2M1 exponent), stored as the E8M0 byte exponent + 127
+           (127 for an all-zero block); elements = E2M1 of x / 2^exponent,
+           round to nearest even, saturating at +-6. Two codes per byte, the
+           even element in the low nibble: W1 [E_l, 2f, d/2] and W2
+           [E_l, d, f/2] uint8, scales [E_l, 2f, d/32] and [E_l, d, f/32]
+           uint8.
 """
 from __future__ import annotations
 
@@ -78,6 +89,8 @@ CONFIGS: Dict[str, MoEConfig] = {
     "mixtral": MoEConfig("mixtral", T=16384, d=4096, f=14336, E_global=8, k=2, e_begin=0, e_end=8, seed=4),
     "deepseek_share_fp8": MoEConfig("deepseek_share_fp8", T=4096, d=7168, f=2048, E_global=256, k=8,
                                     e_begin=0, e_end=32, dtype="fp8_e4m3", num_segments=8, seed=2),
+    "deepseek_share_w4a8": MoEConfig("deepseek_share_w4a8", T=4096, d=7168, f=2048, E_global=256, k=8,
+                                     e_begin=0, e_end=32, dtype="w4a8_mxfp4", num_segments=8, seed=2),
 }
 
 
@@ -103,14 +116,43 @@ def _quant_e4m3_blocks(x: torch.Tensor, br: int, bc: int):
     return q.reshape(R, C).view(torch.uint8), scale.contiguous()
 
 
+# E2M1 rounding boundaries between consecutive magnitudes 0, 0.5, 1, 1.5, 2,
+# 3, 4, 6; at the three marked ties the even code is the upper neighbour.
+_E2M1_BOUNDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_TIE_UP = (0.75, 1.75, 3.5)
+
+
+def _quant_mxfp4_rows(x: torch.Tensor):
+    """Pack a 2-D fp32 tensor [R, K] into MXFP4: (packed codes [R, K/2],
+    E8M0 scale bytes [R, K/32])."""
+    R, K = x.shape
+    assert K % 32 == 0, K
+    xb = x.reshape(R, K // 32, 32)
+    amax = xb.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                    torch.zeros_like(amax))
+    e = e.clamp_(-127, 127)
+    y = (xb / torch.exp2(e)[:, :, None]).abs()
+    bounds = torch.tensor(_E2M1_BOUNDS, dtype=y.dtype, device=y.device)
+    code = torch.bucketize(y, bounds, right=False)
+    for t in _E2M1_TIE_UP:
+        code += (y == t).to(code.dtype)
+    code = code | (torch.signbit(xb).to(code.dtype) << 3)
+    code = code.reshape(R, K).to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
 def generate(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Draw one workload's inputs on `device`.
 
     Returns a dict with
       logits [T, E_global] fp32
       X      [T, d]            bf16, or uint8 e4m3 codes (+ X_scale [T/qb, d/qb] fp32)
-      W1     [E_l, 2f, d]      bf16, or uint8 e4m3 codes (+ W1_scale [E_l, 2f/qb, d/qb])
-      W2     [E_l, d, f]       bf16, or uint8 e4m3 codes (+ W2_scale [E_l, d/qb, f/qb])
+      W1     [E_l, 2f, d]      bf16, or uint8 e4m3 codes (+ W1_scale [E_l, 2f/qb, d/qb]),
+                               or MXFP4: uint8 [E_l, 2f, d/2] (+ W1_scale uint8 [E_l, 2f, d/32])
+      W2     [E_l, d, f]       bf16, or uint8 e4m3 codes (+ W2_scale [E_l, d/qb, f/qb]),
+                               or MXFP4: uint8 [E_l, d, f/2] (+ W2_scale uint8 [E_l, d, f/32])
     """
     device = torch.device(device)
     g = torch.Generator(device=device)
@@ -125,7 +167,8 @@ def generate(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> Dict[s
         logits += prior.to(torch.float32)[None, :]
     out["logits"] = logits.contiguous()
 
-    fp8 = cfg.dtype == "fp8_e4m3"
+    fp8 = cfg.dtype in ("fp8_e4m3", "w4a8_mxfp4")
+    w4 = cfg.dtype == "w4a8_mxfp4"
     qb = cfg.quant_block
     if fp8:
         out["X"], out["X_scale"] = _quant_e4m3_blocks(x32, qb, qb)
@@ -134,14 +177,19 @@ def generate(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> Dict[s
     del x32
 
     for name, rows, cols in (("W1", 2 * f, d), ("W2", d, f)):
-        if fp8:
+        if w4:
+            codes = torch.empty((El, rows, cols // 2), dtype=torch.uint8, device=device)
+            scales = torch.empty((El, rows, cols // 32), dtype=torch.uint8, device=device)
+        elif fp8:
             codes = torch.empty((El, rows, cols), dtype=torch.uint8, device=device)
             scales = torch.empty((El, rows // qb, cols // qb), dtype=torch.float32, device=device)
         else:
             codes = torch.empty((El, rows, cols), dtype=torch.bfloat16, device=device)
         for e in range(El):
             w = _normal(g, (rows, cols), device, std=0.02)
-            if fp8:
+            if w4:
+                codes[e], scales[e] = _quant_mxfp4_rows(w)
+            elif fp8:
                 codes[e], scales[e] = _quant_e4m3_blocks(w, qb, qb)
             else:
                 codes[e] = w.to(torch.bfloat16)

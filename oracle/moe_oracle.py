@@ -41,8 +41,10 @@ Readings where the pages leave a step open (each is also stated where used):
   R7  gate weights are applied in the combine step, not inside Linear-2.
 
 Precision: fp64 throughout except the roundings R6 forces and the fp32
-storage of block scales. Inputs are the exact bf16 / e4m3 bit patterns the
-GPU receives.
+storage of block scales. Inputs are the exact bf16 / e4m3 / MXFP4 bit
+patterns the GPU receives. fp64 is a reading too: the target names an fp32
+oracle; fp64 is the same definition with less rounding of its own, so its
+distance to the GPU result is the GPU's error alone.
 """
 from __future__ import annotations
 
@@ -53,7 +55,8 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "round_to_bf16",
     "e4m3_bits_to_f64", "f64_to_e4m3_bits", "round_to_e4m3",
-    "quantize_rows_e4m3", "route_topk", "dispatch", "swiglu_expert",
+    "quantize_rows_e4m3", "e2m1_to_f64", "e8m0_to_f64", "decode_mxfp4",
+    "route_topk", "dispatch", "swiglu_expert",
     "round_intermediate", "combine", "decode_x", "decode_expert_weights",
     "moe_layer", "moe_layer_bruteforce", "y_row_of_token",
 ]
@@ -158,6 +161,48 @@ def quantize_rows_e4m3(a: np.ndarray, block: int = 128):
     codes = f64_to_e4m3_bits(ab / scale[:, :, None].astype(np.float64))
     deq = e4m3_bits_to_f64(codes) * scale[:, :, None].astype(np.float64)
     return codes.reshape(n, c), scale, deq.reshape(n, c)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 weights (the low-bit weight format of the W4A8 workload), written
+# from the OCP Microscaling (MX) formats definition:
+#   E2M1 element: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent
+#             field 0 is subnormal (m * 0.5); no infinities or NaN; the
+#             magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+#   E8M0 scale: 8 exponent bits, bias 127, no sign or mantissa: 2^(e - 127);
+#             the code 0xFF is NaN.
+#   A block is 32 consecutive elements along K sharing one E8M0 scale:
+#             value = scale * element.
+# Storage (this library's reading, stated in the workload): a weight row of
+# K elements is K/2 bytes, byte j holding element 2j in its low nibble and
+# 2j + 1 in its high nibble; the scales are one byte per row and 32-element
+# block, [rows, K/32].
+# ----------------------------------------------------------------------------
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (0..15)."""
+    c = np.asarray(codes).astype(np.int64)
+    s = np.where(c & 0x8, -1.0, 1.0)
+    E = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(E == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, E - 1))
+    return s * mag
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """Value of E8M0 scale bytes: 2^(e - 127), NaN for 0xFF."""
+    e = np.asarray(codes).astype(np.int64)
+    return np.where(e == 0xFF, np.nan, np.ldexp(1.0, e - 127))
+
+
+def decode_mxfp4(packed, scales, block: int = 32) -> np.ndarray:
+    """Packed MXFP4 rows [rows, K/2] uint8 with E8M0 scales [rows, K/block]
+    -> fp64 [rows, K]."""
+    b = np.asarray(packed).astype(np.uint8)
+    lo, hi = b & 0xF, b >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(b.shape[0], b.shape[1] * 2)
+    sc = np.repeat(e8m0_to_f64(scales), block, axis=-1)
+    return e2m1_to_f64(codes) * sc
 
 
 # ----------------------------------------------------------------------------
@@ -306,7 +351,7 @@ def _block_expand(scale: np.ndarray, block: int) -> np.ndarray:
 def decode_x(inp, cfg, tokens=None) -> np.ndarray:
     """X as fp64 [T, d] (or only the rows in `tokens`)."""
     X = _np(inp["X"])
-    if cfg.dtype == "fp8_e4m3":
+    if cfg.dtype in ("fp8_e4m3", "w4a8_mxfp4"):
         v = e4m3_bits_to_f64(X) * _block_expand(_np(inp["X_scale"]), cfg.quant_block)
     else:
         v = bf16_bits_to_f64(X.view(np.uint16))
@@ -319,7 +364,9 @@ def decode_expert_weights(inp, cfg, e_local: int):
     for name in ("W1", "W2"):
         W = inp[name][e_local]
         Wn = _np(W)
-        if cfg.dtype == "fp8_e4m3":
+        if cfg.dtype == "w4a8_mxfp4":
+            out.append(decode_mxfp4(Wn, _np(inp[name + "_scale"][e_local])))
+        elif cfg.dtype == "fp8_e4m3":
             out.append(e4m3_bits_to_f64(Wn) * _block_expand(_np(inp[name + "_scale"][e_local]), cfg.quant_block))
         else:
             out.append(bf16_bits_to_f64(Wn.view(np.uint16)))
@@ -327,7 +374,7 @@ def decode_expert_weights(inp, cfg, e_local: int):
 
 
 def default_h_mode(cfg) -> str:
-    return "e4m3" if cfg.dtype == "fp8_e4m3" else "bf16"
+    return "e4m3" if cfg.dtype in ("fp8_e4m3", "w4a8_mxfp4") else "bf16"
 
 
 def moe_layer(inp, cfg, h_mode="auto", tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:

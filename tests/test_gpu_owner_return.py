@@ -136,7 +136,9 @@ def test_owner_return_deepseek_share_full_size():
 
 def _overlapped(p, X, g, plan, ws, grid=0):
     """Gather, then the signalling GEMM on the launch stream and the waiting
-    segment copier on a second stream (default priority), started together."""
+    segment copier on a second stream (default priority). The GEMM is
+    enqueued first: where the runtime maps both streams onto one hardware
+    queue, the copier then runs after the GEMM instead of holding it back."""
     R = plan["R"]
     p = padded_problem(p, R)
     main = torch.cuda.current_stream()
@@ -154,9 +156,9 @@ def _overlapped(p, X, g, plan, ws, grid=0):
     ev = torch.cuda.Event()
     ev.record(main)
     side.wait_event(ev)
-    moe.segment_copy_wait(p, O_pad, R, segs, recv, row_done, err, grid, stream=side)
     moe.expert_forward_signal(p, X_pad, None, eo, iota, g["W1"], None, g["W2"], None, O_pad, row_done, ws,
                               stream=main)
+    moe.segment_copy_wait(p, O_pad, R, segs, recv, row_done, err, grid, stream=side)
     main.wait_stream(side)
     torch.cuda.synchronize()
     return recv, int(err.item()), row_done

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "MoEError", "Problem", "WorkspaceLayout", "lib", "make_problem", "workspace_size", "workspace_layout",
-    "workspace_views", "route_topk", "dispatch", "expert_forward", "combine", "layer_forward",
+    "workspace_views", "route_topk", "dispatch", "dispatch_noalloc", "expert_forward", "combine", "layer_forward",
     "check_workspace", "tile_trace", "schedule_of", "store_burst_probe", "owner_plan", "owner_gather",
     "segment_copy", "expert_forward_signal", "segment_copy_wait", "SCHED", "DTYPE", "STATUS",
 ]
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_topk.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [PP] + [_P] * 13 + [ctypes.c_size_t, _P]
+        L.moe_dispatch_noalloc.restype = ctypes.c_int
+        L.moe_dispatch_noalloc.argtypes = [PP] + [_P] * 13
         L.moe_expert_forward.restype = ctypes.c_int
         L.moe_expert_forward.argtypes = [PP] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.moe_combine.restype = ctypes.c_int
@@ -286,6 +288,16 @@ def dispatch(p: Problem, X, X_scale, topk_idx, topk_w, counts, offsets, row_src,
                               _ptr(offsets), _ptr(row_src), _ptr(row_dst), _ptr(tok_off), _ptr(comb_w),
                               _ptr(X_perm), _ptr(X_perm_scale), _ptr(workspace), workspace.numel(),
                               _stream(stream)), "moe_dispatch")
+
+
+def dispatch_noalloc(p: Problem, X, X_scale, topk_idx, topk_w, counts, offsets, row_src, row_dst, tok_off, comb_w,
+                     X_perm, X_perm_scale, stream=None):
+    """moe_dispatch_noalloc: moe_dispatch with the library's own scratch
+    array instead of a workspace (no allocation)."""
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(p), _ptr(X), _ptr(X_scale), _ptr(topk_idx), _ptr(topk_w),
+                                      _ptr(counts), _ptr(offsets), _ptr(row_src), _ptr(row_dst), _ptr(tok_off),
+                                      _ptr(comb_w), _ptr(X_perm), _ptr(X_perm_scale), _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def expert_forward(p: Problem, X_perm, X_perm_scale, offsets, row_dst, W1, W1_scale, W2, W2_scale, combine_buf,

@@ -9,6 +9,8 @@ namespace moe {
 const void* gemm_kernel_bf16();
 const void* gemm_kernel_fp8();
 const void* segment_copy_wait_kernel_ptr();
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 }  // namespace moe
 
 namespace {
@@ -112,6 +114,35 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
                                       topk_idx, topk_w, counts,
                                       offsets, row_src, row_dst, tok_off, comb_w, X_perm, X_perm_scale,
                                       (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X, const float* X_scale,
+                                          const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                                          int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                                          float* comb_w, void* X_perm, float* X_perm_scale, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (!X || !topk_idx || !topk_w || !counts || !offsets || !row_src || !row_dst || !tok_off || !comb_w ||
+      !X_perm)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8 != (X_scale != nullptr) || fp8 != (X_perm_scale != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(X) || !aligned16(X_perm)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe::Layout L = moe::make_layout(*p);
+  // the dispatch's scratch, packed: meta words, per-chunk counts, per-row counts
+  const size_t meta_b = moe::align_up(moe::kMetaInts * 4, 256);
+  const size_t blk_b = moe::align_up((size_t)L.nblk * L.E_l * 4, 256);
+  const size_t tok_b = moe::align_up((size_t)p->T * 4, 256);
+  if (meta_b + blk_b + tok_b > moe::noalloc_scratch_bytes()) return MOE_ERR_UNSUPPORTED;
+  void* base = nullptr;
+  hipError_t e = moe::noalloc_scratch(&base);
+  if (e != hipSuccess) return hip_fail(e);
+  char* sc = static_cast<char*>(base);
+  const moe::DispatchScratch scratch{reinterpret_cast<int32_t*>(sc + meta_b),
+                                     reinterpret_cast<int32_t*>(sc + meta_b + blk_b), reinterpret_cast<int32_t*>(sc)};
+  e = moe::launch_dispatch(*p, L, scratch, X, X_scale, topk_idx, topk_w, counts, offsets, row_src, row_dst, tok_off,
+                           comb_w, X_perm, X_perm_scale, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

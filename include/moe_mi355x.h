@@ -222,6 +222,25 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
                                   float* comb_w, void* X_perm, float* X_perm_scale, void* workspace,
                                   size_t ws_bytes, void* stream);
 
+/* moe_dispatch without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels, with their scratch (per-chunk expert
+ * counts, per-row slot counts, a few status words) in a library-owned device
+ * array of 8 MiB per GPU, created with the library's code object and kept
+ * until the process ends. The call itself allocates nothing. Arguments and
+ * outputs as for moe_dispatch; a problem whose scratch exceeds the array
+ * (about 2 MiB of counts plus 4 bytes per token: more than about 1.5 million
+ * tokens) gives MOE_ERR_UNSUPPORTED before any launch. Every call on one GPU
+ * uses that GPU's one array, so calls that overlap in time on one GPU (two
+ * streams, two host threads) race and give undefined results; calls in
+ * stream order are safe. A routing with more local assignments than the row
+ * capacity shows as offsets[E_l] > cap (rows past it are not stored), as
+ * there is no workspace to carry the error word. */
+MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X, const float* X_scale,
+                                          const int32_t* topk_idx, const float* topk_w, int32_t* counts,
+                                          int32_t* offsets, int32_t* row_src, int32_t* row_dst, int32_t* tok_off,
+                                          float* comb_w, void* X_perm, float* X_perm_scale, void* stream);
+
 /* Grouped expert FFN over the expert-contiguous rows (X-Stage Section 2.2;
  * schedule per p->sched). W1 [E_l, 2f, d], W2 [E_l, d, f] (bf16, or e4m3 codes
  * with W1_scale fp32 [E_l, 2f/128, d/128], W2_scale fp32 [E_l, d/128, f/128]).

@@ -72,10 +72,11 @@ def gemm_bytes(cfg, counts) -> float:
     Linear-2): each local expert with at least one row streams its W1 and W2
     once; per row: X_perm read (d), H write and read (2f), combine-buffer
     write (4d bytes)."""
-    esz = 1 if cfg.dtype == "fp8_e4m3" else 2
+    esz = 1 if cfg.dtype != "bf16" else 2              # activations (e4m3 for fp8 and W4A8)
+    wesz = 0.5 + 1.0 / 32 if cfg.dtype == "w4a8_mxfp4" else esz   # MXFP4: 4-bit codes + an E8M0 byte per 32
     active = sum(1 for c in counts if c > 0)
     A = sum(counts)
-    w = active * 3 * cfg.f * cfg.d * esz
+    w = active * 3 * cfg.f * cfg.d * wesz
     rows = A * (cfg.d * esz + 2 * cfg.f * esz + 4 * cfg.d)
     return float(w + rows)
 
@@ -169,7 +170,7 @@ def main():
     cfg = moe_synth.CONFIGS[args.config]
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    fp8 = cfg.dtype == "fp8_e4m3"
+    fp8 = cfg.dtype != "bf16"   # e4m3 activations: fp8 and W4A8 (MXFP4 weights)
 
     g = moe_synth.generate(cfg, device=dev)
     torch.cuda.synchronize()
@@ -282,7 +283,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02) weights, drawn on the GPU)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E_global": cfg.E_global,
                    "k": cfg.k, "local_experts": [cfg.e_begin, cfg.e_end], "segments": cfg.num_segments,
@@ -375,7 +376,7 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
            "padding_ratio": round(R / max(A, 1), 4), "bands": plan["n_bands"],
            "remote_bands": plan["remote_bands"], "segments": plan["n_segments"],
            "expert_gemm_us_unpadded": round(gemm_std_us, 2)}
-    fp8 = cfg.dtype == "fp8_e4m3"
+    fp8 = cfg.dtype != "bf16"
     cap = moe.row_capacity(p8)
     stream = torch.cuda.current_stream()
     row_src = torch.from_numpy(plan["row_src"]).cuda()

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE_TOO_SMALL",
           4: "MOE_ERR_HIP", 5: "MOE_ERR_DEADLOCK"}
 SCHED = {"expert_wave": 0, "interleaved": 1, "separate": 2, "auto": 3}
-DTYPE = {"bf16": 0, "fp8_e4m3": 1}
+DTYPE = {"bf16": 0, "fp8_e4m3": 1, "w4a8_mxfp4": 2}
 # MOE_FLAG_* of moe_mi355x.h
 FLAG_FP32_Y_DEBUG = 1 << 0
 FLAG_BF16_COMBINE_BUF = 1 << 1
@@ -200,7 +200,7 @@ def workspace_views(p: Problem, ws: torch.Tensor) -> Dict[str, torch.Tensor]:
     L = workspace_layout(p)
     El = p.e_end - p.e_begin
     cap = row_capacity(p)
-    esz = 1 if p.dtype == DTYPE["fp8_e4m3"] else 2
+    esz = 1 if p.dtype != DTYPE["bf16"] else 2   # e4m3 activations for fp8 and W4A8
     edt = torch.uint8 if esz == 1 else torch.bfloat16
     cb_dt = torch.bfloat16 if p.flags & FLAG_BF16_COMBINE_BUF else torch.float32
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["gemm_bf16.hip", "gemm_fp8.hip", "api.hip", "router.hip", "dispatch.hip", "gemm.hip", "combine.hip",
-           "burst.hip", "owner_return.hip", "noalloc.hip"]
+           "burst.hip", "owner_return.hip", "noalloc.hip", "gemm_w4a8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: hipcc -O3 would otherwise emit packed fp32 adds/muls/fmas.

@@ -8,6 +8,7 @@
 namespace moe {
 const void* gemm_kernel_bf16();
 const void* gemm_kernel_fp8();
+const void* gemm_kernel_w4a8();
 const void* segment_copy_wait_kernel_ptr();
 size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** out);
@@ -24,7 +25,8 @@ moe_status_t hip_fail(hipError_t e) {
 
 moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_FP8_E4M3 && p->dtype != MOE_DTYPE_W4A8_MXFP4)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (p->sched < MOE_SCHED_EXPERT_WAVE || p->sched > MOE_SCHED_AUTO) return MOE_ERR_INVALID_ARGUMENT;
   if (p->flags & ~(uint32_t)(MOE_FLAG_FP32_Y_DEBUG | MOE_FLAG_BF16_COMBINE_BUF | MOE_FLAG_TILE_NARROW |
                                 MOE_FLAG_TILE_WIDE | MOE_FLAG_BAND_MAJOR | MOE_FLAG_TILE_TRACE | MOE_FLAG_KEEP_H_F32 |
@@ -41,7 +43,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
   // 32-bit row and element indices inside the kernels
   if ((int64_t)p->T * p->k > (1ll << 30) || cap * p->d > (1ll << 31) - 1 || cap * p->f > (1ll << 31) - 1)
     return MOE_ERR_UNSUPPORTED;
-  if (p->dtype == MOE_DTYPE_FP8_E4M3) {
+  if (p->dtype != MOE_DTYPE_BF16) {
     if (p->quant_block != 128 || p->f % 128 || p->T % 128) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
@@ -60,9 +62,12 @@ bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 
 // wavefronts (two per SIMD): their register counts, as the runtime reports
 // them, rounded up to the allocation granule of 8, within the 512 registers
 // per lane of a SIMD.
-bool copier_fits_beside_gemm(bool fp8) {
+bool copier_fits_beside_gemm(int dtype) {
   hipFuncAttributes g{}, c{};
-  if (hipFuncGetAttributes(&g, fp8 ? moe::gemm_kernel_fp8() : moe::gemm_kernel_bf16()) != hipSuccess) return false;
+  const void* gemm = dtype == MOE_DTYPE_BF16 ? moe::gemm_kernel_bf16()
+                     : dtype == MOE_DTYPE_FP8_E4M3 ? moe::gemm_kernel_fp8() : moe::gemm_kernel_w4a8();
+  const bool fp8 = dtype != MOE_DTYPE_BF16;
+  if (hipFuncGetAttributes(&g, gemm) != hipSuccess) return false;
   if (hipFuncGetAttributes(&c, moe::segment_copy_wait_kernel_ptr()) != hipSuccess) return false;
   auto granule = [](int r) { return (r + 7) / 8 * 8; };
   const int waves_per_simd = moe::gemm_threads(fp8) / 64 / 4;
@@ -102,7 +107,7 @@ MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const void* X, const f
                                   size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   if (!X || !topk_idx || !topk_w || !counts || !offsets || !row_src || !row_dst || !tok_off || !comb_w ||
       !X_perm)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -123,7 +128,7 @@ MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X,
                                           float* comb_w, void* X_perm, float* X_perm_scale, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   if (!X || !topk_idx || !topk_w || !counts || !offsets || !row_src || !row_dst || !tok_off || !comb_w ||
       !X_perm)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -148,11 +153,11 @@ MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X,
 
 MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
                                         const int32_t* offsets, const int32_t* row_dst, const void* W1,
-                                        const float* W1_scale, const void* W2, const float* W2_scale,
+                                        const void* W1_scale, const void* W2, const void* W2_scale,
                                         void* combine_buf, void* workspace, size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   if (!X_perm || !offsets || !row_dst || !W1 || !W2 || !combine_buf) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_perm_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
@@ -177,14 +182,14 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf
 }
 
 MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
-                                       const float* logits, const void* W1, const float* W1_scale,
-                                       const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
+                                       const float* logits, const void* W1, const void* W1_scale,
+                                       const void* W2, const void* W2_scale, void* Y, float* Y_fp32,
                                        void* workspace, size_t ws_bytes, int32_t* topk_idx_out,
                                        float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
                                        int32_t* row_src_out, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   if (!X || !logits || !W1 || !W2 || !Y) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
@@ -291,7 +296,7 @@ MOE_API moe_status_t moe_owner_gather(const moe_problem_t* p, const void* X, con
                                       void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   const int64_t cap = moe::row_capacity(*p);
   if (R < 0 || R > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_scale != nullptr) || fp8 != (X_pad_scale != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
@@ -319,13 +324,13 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
 
 MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
                                                const float* X_perm_scale, const int32_t* offsets,
-                                               const int32_t* row_dst, const void* W1, const float* W1_scale,
-                                               const void* W2, const float* W2_scale, void* combine_buf,
+                                               const int32_t* row_dst, const void* W1, const void* W1_scale,
+                                               const void* W2, const void* W2_scale, void* combine_buf,
                                                int32_t* row_done, int64_t row_done_len, void* workspace,
                                                size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
-  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   if (!X_perm || !offsets || !row_dst || !W1 || !W2 || !combine_buf || !row_done) return MOE_ERR_INVALID_ARGUMENT;
   if (row_done_len < 1 || row_done_len > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARGUMENT;
   if (fp8 != (X_perm_scale != nullptr) || fp8 != (W1_scale != nullptr) || fp8 != (W2_scale != nullptr))
@@ -354,7 +359,7 @@ MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* 
   if (n_segments > 0 && row_done_len < (R + 31) / 32) return MOE_ERR_INVALID_ARGUMENT;
   // A copier wavefront must fit on a SIMD beside the GEMM's two (the fp8
   // GEMM's take the whole register file): otherwise every wait would time out.
-  if (!copier_fits_beside_gemm(p->dtype == MOE_DTYPE_FP8_E4M3)) return MOE_ERR_UNSUPPORTED;
+  if (!copier_fits_beside_gemm(p->dtype)) return MOE_ERR_UNSUPPORTED;
   hipError_t e = moe::launch_segment_copy_wait(*p, O_pad, (int)R, segments, (int)n_segments, recv, (int)R_recv,
                                                row_done, err, grid ? grid : 256, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);

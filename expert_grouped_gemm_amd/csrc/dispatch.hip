@@ -308,7 +308,7 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, const Dispat
                      p.num_segments, L.chunk, p.e_begin, El, L.nblk, L.cap, blk, offsets, tok_off, row_src,
                      row_dst, comb_w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p.dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   const int row_bytes = p.d * (fp8 ? 1 : 2);
   const int blocks = L.cap < 8192 ? (L.cap > 0 ? L.cap : 1) : 8192;
   hipLaunchKernelGGL(dispatch_gather_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(X),

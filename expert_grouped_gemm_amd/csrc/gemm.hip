@@ -217,12 +217,12 @@ int resolve_schedule(const moe_problem_t& p) {
 
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
-                                 const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, void* combine_buf, hipStream_t s, int32_t* row_done,
+                                 const void* W1, const void* W1_scale, const void* W2,
+                                 const void* W2_scale, void* combine_buf, hipStream_t s, int32_t* row_done,
                                  int row_done_len, bool after_dispatch) {
   const int G = gemm_grid(p);
   if (G <= 0) return hipErrorInvalidDevice;
-  const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p.dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   const int sched = resolve_schedule(p);
   GemmParams P{};
   P.X = static_cast<const uint8_t*>(X_perm);
@@ -231,8 +231,11 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   P.H = reinterpret_cast<uint8_t*>(ws + L.pub.h);
   P.C = combine_buf;
   P.Xs = X_perm_scale;
-  P.W1s = W1_scale;
-  P.W2s = W2_scale;
+  const bool w4 = p.dtype == MOE_DTYPE_W4A8_MXFP4;
+  P.W1s = w4 ? nullptr : static_cast<const float*>(W1_scale);
+  P.W2s = w4 ? nullptr : static_cast<const float*>(W2_scale);
+  P.W1e = w4 ? static_cast<const uint8_t*>(W1_scale) : nullptr;
+  P.W2e = w4 ? static_cast<const uint8_t*>(W2_scale) : nullptr;
   P.Hs = fp8 ? reinterpret_cast<float*>(ws + L.pub.h_scale) : nullptr;
   P.Hf = fp8 ? reinterpret_cast<float*>(ws + L.pub.h_f32) : nullptr;
   P.cap = L.cap;
@@ -293,7 +296,7 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
   if (e != hipSuccess) return e;
   auto launch = [&](int mode) {
     P.mode = mode;
-    return fp8 ? launch_gemm_fp8(P, G, s) : launch_gemm_bf16(P, G, s);
+    return w4 ? launch_gemm_w4a8(P, G, s) : fp8 ? launch_gemm_fp8(P, G, s) : launch_gemm_bf16(P, G, s);
   };
   if (sched == MOE_SCHED_SEPARATE) {
     if ((e = launch(MODE_SEP_L1)) != hipSuccess) return e;

@@ -75,8 +75,10 @@ struct GemmParams {
   void* C;                // combine_buf [cap, d]: fp32, or bf16 with c_bf16
   // fp8 only: block scales and the fp32 SwiGLU output before quantisation
   const float* Xs;        // [d/128, cap]  scale of X_perm row r, K block c at c*cap + r
-  const float* W1s;       // [E_l, 2f/128, d/128]
+  const float* W1s;       // [E_l, 2f/128, d/128] (e4m3 weights)
   const float* W2s;       // [E_l, d/128, f/128]
+  const uint8_t* W1e;     // MXFP4 weights: E8M0 scales [E_l, 2f, d/32]
+  const uint8_t* W2e;     // [E_l, d, f/32]
   float* Hs;              // [f/128, cap]
   float* Hf;              // [cap, f] fp32
   int cap;
@@ -109,6 +111,7 @@ struct GemmParams {
 // for occupancy queries.
 hipError_t launch_gemm_bf16(const GemmParams& P, int G, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& P, int G, hipStream_t s);
+hipError_t launch_gemm_w4a8(const GemmParams& P, int G, hipStream_t s);
 const void* gemm_kernel_bf16();
 
 namespace {
@@ -123,6 +126,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int lds_i32;
 
 
 struct Tile {
@@ -136,12 +140,23 @@ struct Tile {
   int nnb;                // width: NNB * 64 weight rows
   int ktiles;             // K bytes / stage_k_bytes
   int krot;               // pipeline stage kt streams K slice (kt + krot) mod ktiles
-  // fp8 only
+  // fp8 activations only
   const float* As;        // row scales of K block 0 for the band's first row (next block: + cap)
-  const float* Sg;        // weight block scales of the first half along K (one per 128-byte stage)
-  const float* Su;        // weight block scales of the second half
+  const float* Sg;        // fp8 weights: block scales of the first half along K (one per 128-byte stage)
+  const float* Su;        // fp8 weights: block scales of the second half
   int cap_stride;         // elements between consecutive K blocks of the row scales
+  // MXFP4 weights only: E8M0 bytes, K/32 per weight row (4 per 128-wide stage)
+  const uint8_t* Eg;      // scale row of the first weight row of the first half
+  const uint8_t* Eu;      // ... of the second half
+  size_t epitch;          // bytes between consecutive scale rows
 };
+
+// Operand types of the expert GEMM (the template parameter OT): bf16
+// activations and weights; e4m3 activations and e4m3 weights with fp32
+// 128x128 block scales; e4m3 activations and MXFP4 weights (E2M1 elements,
+// one E8M0 scale per 32 along K).
+enum OperandType { OT_BF16 = 0, OT_FP8 = 1, OT_W4A8 = 2 };
+__host__ __device__ constexpr bool mxfp4_weights(int OT) { return OT == OT_W4A8; }
 
 // K bytes per row per pipeline stage: 64 bf16 values, or for fp8 one 128-wide
 // scale block of e4m3 values. (64-byte bf16 stages, which double the ring
@@ -149,37 +164,49 @@ struct Tile {
 // and slower on the bandwidth-bound ones.)
 __host__ __device__ constexpr int stage_k_bytes(bool) { return 128; }
 
+// Bytes a weight row contributes to one stage: the stage's K extent (64
+// bf16, or 128 e4m3 values) in the weight format; MXFP4 packs 128 values in
+// 64 bytes.
+__host__ __device__ constexpr int stage_kb_bytes(int OT) { return mxfp4_weights(OT) ? 64 : stage_k_bytes(OT); }
+
 // LDS ring geometry per number of 32-row blocks MB and tile width NNB: a stage
-// holds MB*32 rows of the band plus the NNB*64 weight rows, stage_k_bytes of K
-// each; with fp8 also the 256 row scales of the stage's K block (1 KiB) and
-// the block's two weight scales (padded to 16 bytes).
-__host__ __device__ constexpr int stage_a_bytes(int MB, bool FP8) { return MB * 32 * stage_k_bytes(FP8); }
-__host__ __device__ constexpr int stage_b_bytes(int NNB, bool FP8) { return NNB * 64 * stage_k_bytes(FP8); }
-__host__ __device__ constexpr int stage_bytes(int MB, int NNB, bool FP8) {
-  return stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8) + (FP8 ? kBM * 4 + 16 : 0);
+// holds MB*32 rows of the band plus the NNB*64 weight rows, one stage's K of
+// each; with fp8 activations also the 256 row scales of the stage's K block
+// (1 KiB), and either the block's two fp32 weight scales (padded to 16
+// bytes) or, for MXFP4 weights, one dword of four E8M0 scales per weight row.
+__host__ __device__ constexpr int stage_a_bytes(int MB, int OT) { return MB * 32 * stage_k_bytes(OT); }
+__host__ __device__ constexpr int stage_b_bytes(int NNB, int OT) { return NNB * 64 * stage_kb_bytes(OT); }
+__host__ __device__ constexpr int stage_scale_bytes(int NNB, int OT) {
+  return OT == OT_FP8 ? kBM * 4 + 16 : OT == OT_W4A8 ? kBM * 4 + NNB * 64 * 4 : 0;
 }
-__host__ __device__ constexpr int ring_stages(int MB, int NNB, bool FP8) {
-  return kGemmLds / stage_bytes(MB, NNB, FP8) > 8 ? 8 : kGemmLds / stage_bytes(MB, NNB, FP8);
+__host__ __device__ constexpr int stage_bytes(int MB, int NNB, int OT) {
+  return stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT) + stage_scale_bytes(NNB, OT);
+}
+__host__ __device__ constexpr int ring_stages(int MB, int NNB, int OT) {
+  return kGemmLds / stage_bytes(MB, NNB, OT) > 8 ? 8 : kGemmLds / stage_bytes(MB, NNB, OT);
 }
 // global -> LDS loads issued per lane per stage (16 bytes each, plus one
 // 4-byte row-scale load with fp8)
 // (band rows: a whole number of instructions per wavefront plus, when they
 // do not divide evenly, one partial instruction in every wavefront)
-__host__ __device__ constexpr int stage_a_rows_per_round(bool FP8) {
-  return gemm_threads(FP8) * 16 / stage_k_bytes(FP8);
+__host__ __device__ constexpr int stage_a_rows_per_round(int OT) {
+  return gemm_threads(OT) * 16 / stage_k_bytes(OT);
 }
-__host__ __device__ constexpr int stage_loads(int MB, int NNB, bool FP8) {
-  return (MB * 32 + stage_a_rows_per_round(FP8) - 1) / stage_a_rows_per_round(FP8) +
-         NNB * 64 / stage_a_rows_per_round(FP8) + (FP8 ? 2 : 0);
+__host__ __device__ constexpr int stage_b_rows_per_round(int OT) {
+  return gemm_threads(OT) * 16 / stage_kb_bytes(OT);
+}
+__host__ __device__ constexpr int stage_loads(int MB, int NNB, int OT) {
+  return (MB * 32 + stage_a_rows_per_round(OT) - 1) / stage_a_rows_per_round(OT) +
+         NNB * 64 / stage_b_rows_per_round(OT) + (OT ? 2 : 0);
 }
 
 // Wavefront grid of a tile of width NNB: WM wavefront rows x WN wavefront
 // columns; each wavefront owns CPH = NNB / WN 32-column blocks in each half
 // of the tile's weight rows (half = NNB * 32 rows: the gate rows of a
 // Linear-1 tile, or the first half of a Linear-2 tile's output columns).
-template <int NNB, bool FP8>
+template <int NNB, int OT>
 struct WaveGrid {
-  static constexpr int W = gemm_threads(FP8) / 64;
+  static constexpr int W = gemm_threads(OT) / 64;
   static_assert(W == 4 || W == 8, "wavefront grid");
   static constexpr int WN = (W == 8 && NNB == 4) ? 4 : 2;
   static constexpr int WM = W / WN;
@@ -190,9 +217,9 @@ struct WaveGrid {
 
 // Weight row (tile-relative) of column block c of half h owned by wavefront
 // column wn, for lane row lr; the same index gives the output column.
-template <int NNB, bool FP8>
+template <int NNB, int OT>
 __device__ __forceinline__ int wave_col(int h, int c, int wn, int lr) {
-  return h * (NNB * 32) + (c * WaveGrid<NNB, FP8>::WN + wn) * 32 + lr;
+  return h * (NNB * 32) + (c * WaveGrid<NNB, OT>::WN + wn) * 32 + lr;
 }
 
 // 16-byte chunk c of row `row` in a stage of KB-byte rows. The chunk index is
@@ -201,8 +228,10 @@ __device__ __forceinline__ int wave_col(int h, int c, int wn, int lr) {
 // pair up in a bank line, so the swizzle is (row / 2) mod 8.
 template <int KB>
 __device__ __forceinline__ int chunk_swizzle(int row) {
-  static_assert(KB == 128, "stage row size");
-  return (row >> 1) & 7;
+  static_assert(KB == 128 || KB == 64, "stage row size");
+  // 64-byte rows (MXFP4 weights): four rows share a bank line, and a phase
+  // reads one 16-byte chunk of 16 consecutive rows
+  return KB == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
 }
 template <int KB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -224,42 +253,45 @@ __device__ __forceinline__ void wait_vmcnt() {
 // One pipeline stage: K bytes [kt*KB, kt*KB+KB) of the band's first 32*MB
 // rows and of the tile's NNB*64 weight rows (and, with fp8, the 256 row scales
 // of K block kt and the block's two weight scales), in stage_loads(MB, NNB,
-// FP8) load instructions per lane:
+// OT) load instructions per lane:
 // first the band rows, then the weight rows, then the scales. Lane i of a
 // 16-byte instruction lands at LDS base + 16*i (64/CH rows of KB bytes, CH =
 // KB/16 chunks per row), lane i of a 4-byte instruction at base + 4*i.
 // issue_load issues instruction j of the stage. (Spreading a stage's loads
 // between the MFMAs of the previous stage, instead of issuing them together,
 // was measured no faster.)
-template <int MB, int NNB, bool FP8>
+template <int MB, int NNB, int OT>
 __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
-  constexpr int KB = stage_k_bytes(FP8), CH = KB / 16, RPI = 64 / CH;
-  constexpr int NW = gemm_threads(FP8) / 64, ROUND = NW * RPI;
-  static_assert(ROUND == stage_a_rows_per_round(FP8), "rows per load round");
+  constexpr int KB = stage_k_bytes(OT), CH = KB / 16, RPI = 64 / CH;
+  constexpr int NW = gemm_threads(OT) / 64, ROUND = NW * RPI;
+  static_assert(ROUND == stage_a_rows_per_round(OT), "rows per load round");
+  // weight rows: KBB bytes each (64 for MXFP4), RPIB rows per instruction
+  constexpr int KBB = stage_kb_bytes(OT), CHB = KBB / 16, RPIB = 64 / CHB, ROUNDB = NW * RPIB;
+  static_assert(ROUNDB == stage_b_rows_per_round(OT), "weight rows per load round");
   // NAF full rounds of band rows, then REM rows (a multiple of 32) spread over
   // all wavefronts: REM / NW rows each, the other lanes idle
   constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
-  constexpr int NBW = NNB * 64 / ROUND, half = NNB * 32;
-  static_assert(NBW * ROUND == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
+  constexpr int NBW = NNB * 64 / ROUNDB, half = NNB * 32;
+  static_assert(NBW * ROUNDB == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
   const int w = tid >> 6, lane = tid & 63;
-  const int kb = kt * KB;
-  const int sub = lane / CH, slot = lane % CH;
   if (j < NA) {
     constexpr int RPW = REM / NW;  // rows per wavefront in the partial round
+    const int sub = lane / CH, slot = lane % CH;
     const bool part = REM && j == NAF;
     const int r0 = part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI;
     const int r = r0 + sub;
     const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
-    const uint8_t* g = t.A + (size_t)gr * t.lda + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
+    const uint8_t* g = t.A + (size_t)gr * t.lda + kt * KB + ((slot ^ chunk_swizzle<KB>(r)) << 4);
     if (!part || sub < RPW) __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
   } else if (j < NA + NBW) {
-    const int r0 = ((j - NA) * NW + w) * RPI;
+    const int sub = lane / CHB, slot = lane % CHB;
+    const int r0 = ((j - NA) * NW + w) * RPIB;
     const int r = r0 + sub;
     const uint8_t* base = r < half ? t.Bg : t.Bu;
-    const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kb + ((slot ^ chunk_swizzle<KB>(r)) << 4);
-    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, FP8) + r0 * KB, 16, 0, 0);
-  } else if constexpr (FP8) {
-    lds_t* ss = st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8);
+    const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kt * KBB + ((slot ^ chunk_swizzle<KBB>(r)) << 4);
+    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, OT) + r0 * KBB, 16, 0, 0);
+  } else if constexpr (OT != OT_BF16) {
+    lds_t* ss = st + stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT);
     if (j == NA + NBW) {
       // the 256 row scales: kBM / NW per wavefront, one 4-byte lane each
       constexpr int PER = kBM / NW;
@@ -267,6 +299,14 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
       const int gr = r < t.rows ? r : t.rows - 1;
       const float* g = t.As + (size_t)kt * t.cap_stride + gr;
       if (lane < PER) __builtin_amdgcn_global_load_lds(g, ss + w * PER * 4, 4, 0, 0);
+    } else if constexpr (mxfp4_weights(OT)) {
+      // the weight rows' E8M0 scales of this stage: one dword (four 32-wide
+      // blocks) per weight row, NNB * 64 / NW rows per wavefront
+      constexpr int PERB = NNB * 64 / NW;
+      const int r = w * PERB + lane;
+      const uint8_t* base = r < half ? t.Eg : t.Eu;
+      const uint8_t* g = base + (size_t)(r & (half - 1)) * t.epitch + kt * 4;
+      if (lane < PERB) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4 + w * PERB * 4, 4, 0, 0);
     } else {
       // the block's two weight scales (first and second half of the weight
       // rows) after the row scales. Every wavefront loads them, the same 8
@@ -296,11 +336,11 @@ __device__ __forceinline__ int kslice(const Tile& t, int kt) {
   return s >= t.ktiles ? s - t.ktiles : s;
 }
 
-template <int MB, int NNB, bool FP8>
+template <int MB, int NNB, int OT>
 __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, int tid) {
   const int ks = kslice(t, kt);
 #pragma unroll
-  for (int j = 0; j < stage_loads(MB, NNB, FP8); ++j) issue_load<MB, NNB, FP8>(t, ks, st, tid, j);
+  for (int j = 0; j < stage_loads(MB, NNB, OT); ++j) issue_load<MB, NNB, OT>(t, ks, st, tid, j);
 }
 
 // MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
@@ -381,16 +421,75 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
   }
 }
 
-template <int MB, int NMB, int NNB, bool FP8>
+// MXFP4-weight stage: one 128-wide K block of e4m3 activations against E2M1
+// weights. The scaled MFMA applies each lane's E8M0 byte to the values that
+// lane holds, so in each 64-wide step lane half h (lanes 32h .. 32h + 31)
+// holds 32 consecutive K values of its weight row, elements [32h, 32h + 32)
+// of the step: one MX block, whose scale it passes. The matrix unit pairs
+// the 4-bit operand's first 16 values with K positions [16h, 16h + 16) of
+// the e4m3 operand and its next 16 with [32 + 16h, +16), so the activation
+// fragment of lane half h is chunks h and 2 + h of the step (16 bytes each),
+// not chunks 2h and 2h + 1 as in the fp8 x fp8 product. (Measured on gfx950
+// with one-hot products.) The activation side runs at unit scale and the
+// stage's partial sum is promoted with the row's fp32 activation scale:
+// acc += partial * sx[row].
+template <int NMB, int NNB>
+__device__ __forceinline__ void compute_stage_w4(const lds_t* sa, const lds_t* sb, const lds_t* ss, int tid,
+                                                 f32x16 (&acc)[NMB][WaveGrid<NNB, OT_W4A8>::NCB]) {
+  using G = WaveGrid<NNB, OT_W4A8>;
+  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
+  const int lr = lane & 31, hi = lane >> 5;
+  const f32x16 zero = {};
+  // the scale dword (four E8M0 bytes, one per 32-wide block) of each weight
+  // row this lane holds, read once per stage
+  int sw[G::NCB];
+#pragma unroll
+  for (int nb = 0; nb < G::NCB; ++nb)
+    sw[nb] = *(const lds_i32*)(ss + kBM * 4 + wave_col<NNB, OT_W4A8>(nb / G::CPH, nb % G::CPH, wn, lr) * 4);
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    const int mb = wm + G::WM * mi;
+    f32x16 part[G::NCB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i32x4 a0 = *(const lds_i32x4*)(sa + lds_off<128>(mb * 32 + lr, ks * 4 + hi));
+      const i32x4 a1 = *(const lds_i32x4*)(sa + lds_off<128>(mb * 32 + lr, ks * 4 + 2 + hi));
+      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+      for (int nb = 0; nb < G::NCB; ++nb) {
+        const int row = wave_col<NNB, OT_W4A8>(nb / G::CPH, nb % G::CPH, wn, lr);
+        const i32x4 q = *(const lds_i32x4*)(sb + lds_off<64>(row, ks * 2 + hi));
+        const i32x8 b = {q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+        const int sc = (sw[nb] >> (8 * (ks * 2 + hi))) & 0xFF;
+        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, ks ? part[nb] : zero, 0, 4, 0, 127, 0, sc);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 sx = *(const lds_f32x4*)(ss + (mb * 32 + 8 * g + 4 * hi) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+#pragma unroll
+        for (int nb = 0; nb < G::NCB; ++nb) acc[mi][nb][i] = fmaf(part[nb][i], sx[j], acc[mi][nb][i]);
+      }
+    }
+  }
+}
+
+template <int MB, int NMB, int NNB, int OT>
 __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int kt, int tid,
-                                            f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB]) {
-  if constexpr (FP8) {
+                                            f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB]) {
+  if constexpr (mxfp4_weights(OT)) {
+    const lds_t* ss = st + stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT);
+    compute_stage_w4<NMB, NNB>(st, st + stage_a_bytes(MB, OT), ss, tid, acc);
+  } else if constexpr (OT) {
     static_assert(stage_k_bytes(true) == 128, "an fp8 stage is one 128-wide scale block");
-    const lds_t* ss = st + stage_a_bytes(MB, FP8) + stage_b_bytes(NNB, FP8);
+    const lds_t* ss = st + stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT);
     const float swg = *(const lds_f32*)(ss + kBM * 4), swu = *(const lds_f32*)(ss + kBM * 4 + 4);
-    compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), ss, swg, swu, tid, acc);
+    compute_stage_fp8<NMB, NNB>(st, st + stage_a_bytes(MB, OT), ss, swg, swu, tid, acc);
   } else {
-    compute_stage<NMB, NNB>(st, st + stage_a_bytes(MB, FP8), tid, acc);
+    compute_stage<NMB, NNB>(st, st + stage_a_bytes(MB, OT), tid, acc);
   }
 }
 
@@ -399,13 +498,13 @@ __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int 
 // fp8 Linear-1 tiles of the wide width own a whole 128-column quantisation
 // block: they stage its fp32 SwiGLU values in the (free) LDS ring as
 // [rows][128] floats and quantise from there (quantize_block_lds).
-template <int NNB, bool L1, bool FP8>
-constexpr bool stages_block_in_lds() { return FP8 && L1 && NNB * 32 == 128; }
+template <int NNB, bool L1, int OT>
+constexpr bool stages_block_in_lds() { return OT && L1 && NNB * 32 == 128; }
 
-template <int NMB, int NNB, bool L1, bool FP8>
+template <int NMB, int NNB, bool L1, int OT>
 __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
-                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, FP8>::NCB], lds_t* lds) {
-  using G = WaveGrid<NNB, FP8>;
+                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
+  using G = WaveGrid<NNB, OT>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -421,13 +520,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
           for (int c = 0; c < G::CPH; ++c) {
             const float g = acc[mi][c][i], u = acc[mi][G::CPH + c][i];
             const float act = g / (1.0f + expf(-g)) * u;
-            const int cb = wave_col<NNB, FP8>(0, c, wn, lr);
+            const int cb = wave_col<NNB, OT>(0, c, wn, lr);
             const int col = t.n * (NNB * 32) + cb;
             const size_t at = (size_t)(t.row0 + m) * P.f + col;
-            if constexpr (stages_block_in_lds<NNB, L1, FP8>()) {
+            if constexpr (stages_block_in_lds<NNB, L1, OT>()) {
               reinterpret_cast<__attribute__((address_space(3))) float*>(lds)[m * 128 + cb] = act;
               if (P.keep_hf) P.Hf[at] = act;
-            } else if constexpr (FP8) {
+            } else if constexpr (OT) {
               P.Hf[at] = act;  // quantised per 128-column block once both halves are stored
             } else {
               reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
@@ -441,13 +540,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
             if (P.c_bf16) {
 #pragma unroll
               for (int nb = 0; nb < G::NCB; ++nb) {
-                const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
+                const int col = t.n * (NNB * 64) + wave_col<NNB, OT>(nb / G::CPH, nb % G::CPH, wn, lr);
                 reinterpret_cast<uint16_t*>(P.C)[(size_t)dst * P.d + col] = f32_to_bf16_rne(acc[mi][nb][i]);
               }
             } else {
 #pragma unroll
               for (int nb = 0; nb < G::NCB; ++nb) {
-                const int col = t.n * (NNB * 64) + wave_col<NNB, FP8>(nb / G::CPH, nb % G::CPH, wn, lr);
+                const int col = t.n * (NNB * 64) + wave_col<NNB, OT>(nb / G::CPH, nb % G::CPH, wn, lr);
                 reinterpret_cast<float*>(P.C)[(size_t)dst * P.d + col] = acc[mi][nb][i];
               }
             }
@@ -463,14 +562,14 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
 
 // Drain the last R+1 stages of the ring: stage kt is complete once at most R
 // stages (R * stage_loads loads per lane) are still in flight.
-template <int MB, int NMB, int NNB, bool FP8, int R>
+template <int MB, int NMB, int NNB, int OT, int R>
 __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt, int tid,
-                                      f32x16 (&acc)[NMB > 0 ? NMB : 1][WaveGrid<NNB, FP8>::NCB]) {
-  constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8);
-  wait_vmcnt<R * stage_loads(MB, NNB, FP8)>();
+                                      f32x16 (&acc)[NMB > 0 ? NMB : 1][WaveGrid<NNB, OT>::NCB]) {
+  constexpr int S = ring_stages(MB, NNB, OT), SB = stage_bytes(MB, NNB, OT);
+  wait_vmcnt<R * stage_loads(MB, NNB, OT)>();
   lds_barrier();
-  if constexpr (NMB > 0) compute_any<MB, NMB, NNB, FP8>(t, lds + rd * SB, kt, tid, acc);
-  if constexpr (R > 0) drain<MB, NMB, NNB, FP8, R - 1>(t, lds, rd + 1 == S ? 0 : rd + 1, kt + 1, tid, acc);
+  if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
+  if constexpr (R > 0) drain<MB, NMB, NNB, OT, R - 1>(t, lds, rd + 1 == S ? 0 : rd + 1, kt + 1, tid, acc);
 }
 
 // The whole tile: every wavefront runs the same loads and barriers and owns
@@ -482,31 +581,31 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // are then computed once per tile instead of being hoisted, for every tile
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
-template <int MB, int NMB, int NNB, bool L1, bool FP8>
+template <int MB, int NMB, int NNB, bool L1, int OT>
 __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  constexpr int S = ring_stages(MB, NNB, FP8), SB = stage_bytes(MB, NNB, FP8), LD = stage_loads(MB, NNB, FP8);
+  constexpr int S = ring_stages(MB, NNB, OT), SB = stage_bytes(MB, NNB, OT), LD = stage_loads(MB, NNB, OT);
   static_assert(S >= 2, "the LDS ring needs two stages");
-  f32x16 acc[NMB > 0 ? NMB : 1][WaveGrid<NNB, FP8>::NCB];
+  f32x16 acc[NMB > 0 ? NMB : 1][WaveGrid<NNB, OT>::NCB];
 #pragma unroll
   for (int a = 0; a < (NMB > 0 ? NMB : 1); ++a)
 #pragma unroll
-    for (int b = 0; b < WaveGrid<NNB, FP8>::NCB; ++b)
+    for (int b = 0; b < WaveGrid<NNB, OT>::NCB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
   const int KT = t.ktiles;
   if (KT < S) {
     // the whole K extent fits in the ring
-    for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, FP8>(t, kt, lds + kt * SB, tid);
+    for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
     wait_vmcnt<0>();
     lds_barrier();
     if constexpr (NMB > 0)
-      for (int kt = 0; kt < KT; ++kt) compute_any<MB, NMB, NNB, FP8>(t, lds + kt * SB, kt, tid, acc);
+      for (int kt = 0; kt < KT; ++kt) compute_any<MB, NMB, NNB, OT>(t, lds + kt * SB, kt, tid, acc);
   } else {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, FP8>(t, s, lds + s * SB, tid);
+    for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
     int rd = 0, wr = S - 1, kt = 0;
     for (; kt + S - 1 < KT; ++kt) {
       // Slot wr held stage kt-1, which every wavefront finished reading
@@ -514,19 +613,19 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
       // so S-1 stages stay in flight while this one is awaited (the memory
       // system bounds the requests a CU may have outstanding; letting the
       // queue drain at every step would waste that bound).
-      issue_stage<MB, NNB, FP8>(t, kt + S - 1, lds + wr * SB, tid);
+      issue_stage<MB, NNB, OT>(t, kt + S - 1, lds + wr * SB, tid);
       wait_vmcnt<(S - 1) * LD>();  // this lane's loads of stage kt have landed
       lds_barrier();               // ... everyone's
-      if constexpr (NMB > 0) compute_any<MB, NMB, NNB, FP8>(t, lds + rd * SB, kt, tid, acc);
+      if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
       lds_barrier();               // slot rd is free for the refill of the next step
       rd = rd + 1 == S ? 0 : rd + 1;
       wr = wr + 1 == S ? 0 : wr + 1;
     }
-    drain<MB, NMB, NNB, FP8, S - 2>(t, lds, rd, kt, tid, acc);
+    drain<MB, NMB, NNB, OT, S - 2>(t, lds, rd, kt, tid, acc);
   }
   lds_barrier();  // LDS ring free for the next tile
   if (P.trace) t_main = __builtin_amdgcn_s_memrealtime();
-  if constexpr (NMB > 0) epilogue<NMB, NNB, L1, FP8>(P, t, tid, acc, lds);
+  if constexpr (NMB > 0) epilogue<NMB, NNB, L1, OT>(P, t, tid, acc, lds);
 }
 
 // MB = the band's 32-row blocks. With two wavefront rows (WM = 2) wavefront
@@ -536,35 +635,35 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, ld
 // band fit in the LDS where 192-row ones would leave two. With four
 // wavefront rows MB is rounded up to a multiple of 4 (rows past the band
 // re-read its last row and are not stored).
-template <int MB, int NNB, bool L1, bool FP8>
+template <int MB, int NNB, bool L1, int OT>
 __device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
-  constexpr int WM = WaveGrid<NNB, FP8>::WM;
+  constexpr int WM = WaveGrid<NNB, OT>::WM;
   if constexpr (WM == 2 && (MB & 1)) {
-    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, FP8>(P, t, lds, t_main);
-    else tile_body<MB, MB / 2, NNB, L1, FP8>(P, t, lds, t_main);
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT>(P, t, lds, t_main);
+    else tile_body<MB, MB / 2, NNB, L1, OT>(P, t, lds, t_main);
   } else {
     static_assert(MB % WM == 0, "row blocks per wavefront row");
-    tile_body<MB, MB / WM, NNB, L1, FP8>(P, t, lds, t_main);
+    tile_body<MB, MB / WM, NNB, L1, OT>(P, t, lds, t_main);
   }
 }
 
-template <int NNB, bool L1, bool FP8>
+template <int NNB, bool L1, int OT>
 __device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
-  if constexpr (WaveGrid<NNB, FP8>::WM == 2) {
+  if constexpr (WaveGrid<NNB, OT>::WM == 2) {
     switch ((t.rows + 31) >> 5) {
-      case 1: run_tile<1, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 2: run_tile<2, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 3: run_tile<3, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 4: run_tile<4, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 5: run_tile<5, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 6: run_tile<6, NNB, L1, FP8>(P, t, lds, t_main); break;
-      case 7: run_tile<7, NNB, L1, FP8>(P, t, lds, t_main); break;
-      default: run_tile<8, NNB, L1, FP8>(P, t, lds, t_main); break;
+      case 1: run_tile<1, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 2: run_tile<2, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 3: run_tile<3, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 4: run_tile<4, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 5: run_tile<5, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 6: run_tile<6, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 7: run_tile<7, NNB, L1, OT>(P, t, lds, t_main); break;
+      default: run_tile<8, NNB, L1, OT>(P, t, lds, t_main); break;
     }
   } else {
-    static_assert(WaveGrid<NNB, FP8>::WM == 4, "wavefront rows");
-    if (t.rows <= 128) run_tile<4, NNB, L1, FP8>(P, t, lds, t_main);
-    else run_tile<8, NNB, L1, FP8>(P, t, lds, t_main);
+    static_assert(WaveGrid<NNB, OT>::WM == 4, "wavefront rows");
+    if (t.rows <= 128) run_tile<4, NNB, L1, OT>(P, t, lds, t_main);
+    else run_tile<8, NNB, L1, OT>(P, t, lds, t_main);
   }
 }
 
@@ -675,9 +774,9 @@ __device__ void quantize_block(const GemmParams& P, int row0, int rows, int j) {
 // published) quantises it. In the fused schedules the quantised block is
 // counted in l2_full[p]; the band is ready at f / 128. The separate schedule
 // needs no counting for Linear-2: its launch starts after this one ends.
-template <bool FP8>
+template <int OT>
 __device__ __forceinline__ void finish_l1_tile(const GemmParams& P, const Tile& t, int p, bool fused, lds_t* lds) {
-  if constexpr (!FP8) {
+  if constexpr (!OT) {
     if (fused) publish(P.l2_full + p, 1);
   } else {
     const int bn1 = t.nnb * 32;
@@ -748,9 +847,9 @@ __device__ __forceinline__ void record_tile(const GemmParams& P, bool l1, int p,
   }
 }
 
-template <bool L1, bool FP8>
+template <bool L1, int OT>
 __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int nnb, bool fused, lds_t* lds) {
-  constexpr int esz = FP8 ? 1 : 2;
+  constexpr int esz = OT ? 1 : 2;
   uint64_t t_start = 0, t_ready = 0, t_main = 0;
   if (P.trace) t_start = __builtin_amdgcn_s_memrealtime();
   Tile t;
@@ -760,17 +859,25 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
   t.n = n;
   t.nnb = nnb;
   t.cap_stride = P.cap;
+  // weight rows: K elements of esz bytes, or K/2 bytes of packed MXFP4
+  constexpr bool W4 = mxfp4_weights(OT);
   if constexpr (L1) {
     const int bn = nnb * 32;  // SwiGLU columns: bn gate rows and bn up rows
     t.lda = (size_t)P.d * esz;
-    t.ldb = (size_t)P.d * esz;
+    t.ldb = W4 ? (size_t)P.d / 2 : (size_t)P.d * esz;
     t.A = P.X + (size_t)t.row0 * t.lda;
     const uint8_t* We = P.W1 + (size_t)e * 2 * P.f * t.ldb;
     t.Bg = We + (size_t)(n * bn) * t.ldb;
     t.Bu = We + (size_t)(P.f + n * bn) * t.ldb;
-    t.ktiles = P.d * esz / stage_k_bytes(FP8);
+    t.ktiles = P.d * esz / stage_k_bytes(OT);
     t.krot = 0;
-    if constexpr (FP8) {
+    if constexpr (W4) {
+      t.As = P.Xs + t.row0;
+      t.epitch = (size_t)P.d / 32;
+      const uint8_t* Es = P.W1e + (size_t)e * 2 * P.f * t.epitch;
+      t.Eg = Es + (size_t)(n * bn) * t.epitch;
+      t.Eu = Es + (size_t)(P.f + n * bn) * t.epitch;
+    } else if constexpr (OT) {
       const int db = P.d >> 7, fb2 = (2 * P.f) >> 7;
       t.As = P.Xs + t.row0;
       t.Sg = P.W1s + ((size_t)e * fb2 + (n * bn) / 128) * db;
@@ -779,13 +886,18 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
   } else {
     const int bn = nnb * 64;  // output columns
     t.lda = (size_t)P.f * esz;
-    t.ldb = (size_t)P.f * esz;
+    t.ldb = W4 ? (size_t)P.f / 2 : (size_t)P.f * esz;
     t.A = P.H + (size_t)t.row0 * t.lda;
     t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * bn) * t.ldb;
     t.Bu = t.Bg + (size_t)(bn / 2) * t.ldb;
-    t.ktiles = P.f * esz / stage_k_bytes(FP8);
+    t.ktiles = P.f * esz / stage_k_bytes(OT);
     t.krot = (e * kKRot) % t.ktiles;
-    if constexpr (FP8) {
+    if constexpr (W4) {
+      t.As = P.Hs + t.row0;
+      t.epitch = (size_t)P.f / 32;
+      t.Eg = P.W2e + ((size_t)e * P.d + (size_t)n * bn) * t.epitch;
+      t.Eu = t.Eg + (size_t)(bn / 2) * t.epitch;
+    } else if constexpr (OT) {
       t.As = P.Hs + t.row0;
       t.Sg = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn) / 128) * (P.f >> 7);
       t.Su = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn + bn / 2) / 128) * (P.f >> 7);
@@ -793,9 +905,9 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
     if (fused) wait_row_ready(P, p);
   }
   if (P.trace) t_ready = __builtin_amdgcn_s_memrealtime();
-  if (nnb == 4) dispatch_tile<4, L1, FP8>(P, t, lds, t_main);
-  else dispatch_tile<2, L1, FP8>(P, t, lds, t_main);
-  if constexpr (L1) finish_l1_tile<FP8>(P, t, p, fused, lds);
+  if (nnb == 4) dispatch_tile<4, L1, OT>(P, t, lds, t_main);
+  else dispatch_tile<2, L1, OT>(P, t, lds, t_main);
+  if constexpr (L1) finish_l1_tile<OT>(P, t, p, fused, lds);
   if constexpr (!L1) {
     if (P.row_done) finish_l2_tile(P, t);
   }
@@ -821,7 +933,7 @@ __device__ __forceinline__ void raster(int i, int nb, int N, int gm, int& p, int
 // fewer than G tiles), that tail runs as twice as many half-width tiles:
 // wide tile n of a band is exactly narrow tiles 2n and 2n+1, with the same K
 // order, so the last round keeps every workgroup busy for half as long.
-template <bool L1, bool FP8>
+template <bool L1, int OT>
 __device__ __forceinline__ void separate_tiles(const GemmParams& P, int nb, int N, int nnb, int lid, int G,
                                                lds_t* lds) {
   const int total = nb * N;
@@ -831,17 +943,17 @@ __device__ __forceinline__ void separate_tiles(const GemmParams& P, int nb, int 
   for (int i = lid; i < end; i += G) {
     if (i < cut) {
       raster(i, nb, N, P.group_m, p, n);
-      do_tile<L1, FP8>(P, p, n, nnb, false, lds);
+      do_tile<L1, OT>(P, p, n, nnb, false, lds);
     } else {
       const int j = i - cut;
       raster(cut + (j >> 1), nb, N, P.group_m, p, n);
-      do_tile<L1, FP8>(P, p, 2 * n + (j & 1), 2, false, lds);
+      do_tile<L1, OT>(P, p, 2 * n + (j & 1), 2, false, lds);
     }
   }
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmParams P) {
+template <int OT>
+__global__ __launch_bounds__(gemm_threads(OT), 1) void moe_gemm_kernel(GemmParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   lds_t* lds = (lds_t*)smem;  // address-space cast to the LDS window
   const int G = gridDim.x;
@@ -853,10 +965,10 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
   int p, n;
   switch (P.mode) {
     case MODE_SEP_L1:
-      separate_tiles<true, FP8>(P, Pb, P.N1, P.nnb1, lid, G, lds);
+      separate_tiles<true, OT>(P, Pb, P.N1, P.nnb1, lid, G, lds);
       break;
     case MODE_SEP_L2:
-      separate_tiles<false, FP8>(P, Pb, P.N2, P.nnb2, lid, G, lds);
+      separate_tiles<false, OT>(P, Pb, P.N2, P.nnb2, lid, G, lds);
       break;
     case MODE_WAVE: {
       const int nw = P.meta[META_NWAVES];
@@ -864,11 +976,11 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
         const int pb0 = P.wave_band0[wv], pb1 = P.wave_band0[wv + 1];
         for (int i = lid; i < (pb1 - pb0) * P.N1; i += G) {
           raster(i, pb1 - pb0, P.N1, P.group_m, p, n);
-          do_tile<true, FP8>(P, pb0 + p, n, P.nnb1, true, lds);
+          do_tile<true, OT>(P, pb0 + p, n, P.nnb1, true, lds);
         }
         for (int i = lid; i < (pb1 - pb0) * P.N2; i += G) {
           raster(i, pb1 - pb0, P.N2, P.group_m, p, n);
-          do_tile<false, FP8>(P, pb0 + p, n, P.nnb2, true, lds);
+          do_tile<false, OT>(P, pb0 + p, n, P.nnb2, true, lds);
         }
       }
       break;
@@ -891,13 +1003,13 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
         if (k2 < cut2) raster(k2, Pb, P2, P.group_m, p2, c2);
         if (k2 < cut2 && p2 + P.lead_D <= b1) {
           const int n = 2 * c2 + r;
-          if (n < P.N2) do_tile<false, FP8>(P, p2, n, P.nnb2, true, lds);
+          if (n < P.N2) do_tile<false, OT>(P, p2, n, P.nnb2, true, lds);
           k2 += Gp;
         } else {
           int p1, c1;
           raster(k1, Pb, P1, P.group_m, p1, c1);
           const int n = 2 * c1 + r;
-          if (n < P.N1) do_tile<true, FP8>(P, p1, n, P.nnb1, true, lds);
+          if (n < P.N1) do_tile<true, OT>(P, p1, n, P.nnb1, true, lds);
           k1 += Gp;
         }
       }
@@ -909,7 +1021,7 @@ __global__ __launch_bounds__(gemm_threads(FP8), 1) void moe_gemm_kernel(GemmPara
       for (int j = lid; j < 4 * (end2 - cut2); j += G) {
         int p2, c2;
         raster(cut2 + (j >> 2), Pb, P2, P.group_m, p2, c2);
-        if (2 * c2 + ((j >> 1) & 1) < P.N2) do_tile<false, FP8>(P, p2, 4 * c2 + (j & 3), 2, true, lds);
+        if (2 * c2 + ((j >> 1) & 1) < P.N2) do_tile<false, OT>(P, p2, 4 * c2 + (j & 3), 2, true, lds);
       }
       break;
     }

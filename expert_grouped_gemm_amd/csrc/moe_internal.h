@@ -78,7 +78,7 @@ inline Layout make_layout(const moe_problem_t& p) {
   Layout L{};
   const int El = p.e_end - p.e_begin;
   const int64_t cap = row_capacity(p);
-  const bool fp8 = p.dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = p.dtype != MOE_DTYPE_BF16;  // e4m3 activations (and their scales)
   const size_t esz = fp8 ? 1 : 2;
   L.cap = (int)cap;
   L.E_l = El;
@@ -142,8 +142,8 @@ hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, const Dispat
 
 hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* ws, const void* X_perm,
                                  const float* X_perm_scale, const int32_t* offsets, const int32_t* row_dst,
-                                 const void* W1, const float* W1_scale, const void* W2,
-                                 const float* W2_scale, void* combine_buf, hipStream_t s,
+                                 const void* W1, const void* W1_scale, const void* W2,
+                                 const void* W2_scale, void* combine_buf, hipStream_t s,
                                  int32_t* row_done = nullptr, int row_done_len = 0, bool after_dispatch = false);
 
 hipError_t launch_combine(const moe_problem_t& p, const void* combine_buf, const int32_t* tok_off,

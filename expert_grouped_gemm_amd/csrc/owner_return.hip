@@ -236,7 +236,7 @@ hipError_t launch_owner_gather(const moe_problem_t& p, const void* X, const floa
                                int R, void* X_pad, float* X_pad_scale, int cap, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int blocks = R < 8192 ? R : 8192;
-  if (p.dtype == MOE_DTYPE_FP8_E4M3) {
+  if (p.dtype != MOE_DTYPE_BF16) {
     hipLaunchKernelGGL(owner_gather_fp8_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(X),
                        X_scale, row_src, R, p.T * p.k, p.k, p.d, cap, static_cast<uint8_t*>(X_pad), X_pad_scale);
     return hipGetLastError();

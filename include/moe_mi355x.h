@@ -68,8 +68,12 @@ typedef enum {
 
 typedef enum {
   MOE_DTYPE_BF16 = 0,             /* X, W1, W2 bfloat16; H bfloat16 */
-  MOE_DTYPE_FP8_E4M3 = 1          /* X, W1, W2 OCP E4M3FN codes with fp32 block scales; H e4m3 with
+  MOE_DTYPE_FP8_E4M3 = 1,         /* X, W1, W2 OCP E4M3FN codes with fp32 block scales; H e4m3 with
                                      one fp32 scale per row and 128 columns */
+  MOE_DTYPE_W4A8_MXFP4 = 2        /* X e4m3 with fp32 block scales as above (H too); W1, W2 in OCP MXFP4:
+                                     E2M1 codes, two per byte (the even element in the low nibble), and
+                                     one E8M0 scale byte per 32 consecutive elements along K. The
+                                     low-bit weight variant (W4A8) of X-Stage's evaluation, Section 5 */
 } moe_dtype_t;
 
 /* Tile schedule of the grouped expert GEMMs (X-Stage, Section 4.2 "MegaMoE:
@@ -243,7 +247,9 @@ MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X,
 
 /* Grouped expert FFN over the expert-contiguous rows (X-Stage Section 2.2;
  * schedule per p->sched). W1 [E_l, 2f, d], W2 [E_l, d, f] (bf16, or e4m3 codes
- * with W1_scale fp32 [E_l, 2f/128, d/128], W2_scale fp32 [E_l, d/128, f/128]).
+ * with W1_scale fp32 [E_l, 2f/128, d/128], W2_scale fp32 [E_l, d/128, f/128];
+ * MXFP4: W1 uint8 [E_l, 2f, d/2], W2 uint8 [E_l, d, f/2] with W1_scale uint8
+ * E8M0 [E_l, 2f, d/32], W2_scale uint8 E8M0 [E_l, d, f/32]).
  * Writes combine_buf [cap, d] (fp32, or bf16 with MOE_FLAG_BF16_COMBINE_BUF):
  * row row_dst[r] = W2[e] act(r). The intermediate H lives in the workspace.
  * offsets/row_dst as from moe_dispatch. Device-side checks (reported by
@@ -253,7 +259,7 @@ MOE_API moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* X,
  * outside [0, cap) is not stored. */
 MOE_API moe_status_t moe_expert_forward(const moe_problem_t* p, const void* X_perm, const float* X_perm_scale,
                                         const int32_t* offsets, const int32_t* row_dst, const void* W1,
-                                        const float* W1_scale, const void* W2, const float* W2_scale,
+                                        const void* W1_scale, const void* W2, const void* W2_scale,
                                         void* combine_buf, void* workspace, size_t ws_bytes, void* stream);
 
 /* Weighted combine (Cui et al. Section 2.1 step (5)): Y bf16 [T, d] in
@@ -281,8 +287,8 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf
  * unwritten. Every other intermediate is left in the workspace at
  * moe_workspace_get_layout's offsets. */
 MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
-                                       const float* logits, const void* W1, const float* W1_scale,
-                                       const void* W2, const float* W2_scale, void* Y, float* Y_fp32,
+                                       const float* logits, const void* W1, const void* W1_scale,
+                                       const void* W2, const void* W2_scale, void* Y, float* Y_fp32,
                                        void* workspace, size_t ws_bytes, int32_t* topk_idx_out,
                                        float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
                                        int32_t* row_src_out, void* stream);
@@ -392,8 +398,8 @@ MOE_API moe_status_t moe_segment_copy(const moe_problem_t* p, const float* O_pad
  * out (the fp8 GEMM, at 256 registers per wavefront, is such a case). */
 MOE_API moe_status_t moe_expert_forward_signal(const moe_problem_t* p, const void* X_perm,
                                                const float* X_perm_scale, const int32_t* offsets,
-                                               const int32_t* row_dst, const void* W1, const float* W1_scale,
-                                               const void* W2, const float* W2_scale, void* combine_buf,
+                                               const int32_t* row_dst, const void* W1, const void* W1_scale,
+                                               const void* W2, const void* W2_scale, void* combine_buf,
                                                int32_t* row_done, int64_t row_done_len, void* workspace,
                                                size_t ws_bytes, void* stream);
 MOE_API moe_status_t moe_segment_copy_wait(const moe_problem_t* p, const float* O_pad, int64_t R,

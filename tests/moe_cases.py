@@ -9,8 +9,8 @@ roundings the data path forces: bf16 inputs, H rounded to bf16):
   * on the bf16 Y the same max-abs bound after allowing the one bf16 ulp of
     Y_ref that rounding the exact sum can already cost: max(|Y - Y_ref| -
     ulp_bf16(Y_ref)) <= 1e-2 * rms(Y_ref).
-fp8: relative Frobenius <= 3e-2 against the oracle that quantises H to e4m3
-with per-row 128-column scales.
+fp8 and W4A8 (e4m3 activations): relative Frobenius <= 3e-2 against the
+oracle that quantises H to e4m3 with per-row 128-column scales.
 """
 from __future__ import annotations
 

@@ -230,6 +230,16 @@ def main():
     wall = time.perf_counter() - t0
     moe.check_workspace(p, ws)
 
+    # Outside the timed steps, the same box: the four component calls back to
+    # back (no events), the launch chain the fused call replaces.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    chain_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    moe.check_workspace(p, ws)
+
     # Outside the timed steps: the same steps with an event between stages for
     # the stage breakdown (each event record leaves the stream idle for a few
     # microseconds, so these steps run slower than the timed ones), then the
@@ -245,6 +255,8 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     moe.check_workspace(p, ws)
+
+    stage_proto = stage_protocol(moe, cfg, p, g, v, ws, Y, stream)
 
     stage_names = ["route", "dispatch", "expert_gemm", "combine"]
     per = {n: [events[i][j].elapsed_time(events[i][j + 1]) * 1e3 for i in range(args.steps)]
@@ -291,10 +303,23 @@ def main():
                    "band_major": args.band_major,
                    "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "component_calls_ms_per_step": round(chain_ms, 4),
+        "component_calls_note": "the same step as moe_route_topk, moe_dispatch, moe_expert_forward and moe_combine "
+                                "back to back (the launch chain the fused moe_layer_forward replaces), same process",
         "stages_us_median": {n: round(x, 2) for n, x in med.items()},
         "stages_note": "from separate steps with an event between stages, after the timed steps",
-        "dispatch_GBps": round(disp_bytes / (med["dispatch"] * 1e-6) / 1e9, 1),
-        "combine_GBps": round(comb_bytes / (med["combine"] * 1e-6) / 1e9, 1),
+        "dispatch_GBps": round(disp_bytes / (stage_proto["dispatch"]["median_us"] * 1e-6) / 1e9, 1),
+        "combine_GBps": round(comb_bytes / (stage_proto["combine"]["median_us"] * 1e-6) / 1e9, 1),
+        "dispatch_combine_protocol": dict(
+            stage_proto,
+            algorithmic_bytes={"dispatch": disp_bytes, "combine": comb_bytes},
+            frac_of_hbm_peak={"dispatch": round(disp_bytes / (stage_proto["dispatch"]["median_us"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBPS, 4),
+                              "combine": round(comb_bytes / (stage_proto["combine"]["median_us"] * 1e-6) / 1e9
+                                               / HBM_PEAK_GBPS, 4)},
+            note="moe_dispatch and moe_combine each timed alone, 20 trials after one warm-up call, a 512 MiB "
+                 "write before every trial flushing the 256 MiB last-level cache; copy_GBps is a device-to-device "
+                 "copy of the combine's byte count under the same protocol (the achievable streaming rate)"),
         "roofline": {
             "kernel": "moe_gemm_kernel (grouped Linear-1+SwiGLU+Linear-2, one persistent launch)"
             if moe.schedule_of(p) != "separate" else "moe_gemm_kernel (Linear-1 launch + Linear-2 launch)",
@@ -482,6 +507,48 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
     return res
 
 
+def stage_protocol(moe, cfg, p, g, v, ws, Y, stream, trials=20):
+    """moe_dispatch and moe_combine timed standalone: one warm-up call, then
+    `trials` trials each preceded by a 512 MiB write that flushes the 256 MiB
+    last-level cache, HIP events on the launch stream around the call alone;
+    median, p10 and p90 in microseconds. A device-to-device copy of the
+    combine's algorithmic byte count (read + write) is timed the same way."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    esz = 1 if cfg.dtype != "bf16" else 2
+    A = int(v["offsets"][-1])
+    comb_bytes = A * cfg.d * 4 + cfg.T * cfg.d * 2
+    half = comb_bytes // 2 // 16 * 16
+    src = torch.empty(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    calls = {
+        "dispatch": lambda: moe.dispatch(p, g["X"], g.get("X_scale"), v["topk_idx"], v["topk_w"], v["counts"],
+                                         v["offsets"], v["row_src"], v["row_dst"], v["tok_off"], v["comb_w"],
+                                         v["x_perm"], v.get("x_perm_scale"), ws, stream),
+        "combine": lambda: moe.combine(p, v["combine_buf"], v["tok_off"], v["comb_w"], Y, None, stream),
+        "copy": lambda: dst.copy_(src),
+    }
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        us = []
+        for _ in range(trials):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        a = np.array(us)
+        out[name] = {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+                     "p90_us": round(float(np.percentile(a, 90)), 2)}
+    out["copy_GBps"] = round(2 * half / (out["copy"]["median_us"] * 1e-6) / 1e9, 1)
+    moe.check_workspace(p, ws)
+    return out
+
+
 def cpu_baseline(cfg, g, args):
     """The oracle (fp64 NumPy) as it stands, timed on this host on a bounded
     sample: routing and dispatch of all T tokens plus the expert FFNs and the
@@ -507,7 +574,19 @@ def cpu_baseline(cfg, g, args):
         n *= 2
     A_s = int(np.sum(r["row_src"] // cfg.k < n))
     flop = 6.0 * A_s * cfg.d * cfg.f
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:
+        blas = "unknown"
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"first {n} of {cfg.T} tokens ({A_s} local assignments; routing+dispatch of all tokens), "
                       f"{dt:.1f} s"}
 

@@ -212,15 +212,17 @@ MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, co
   int32_t* counts = counts_out ? counts_out : I(W.counts);
   int32_t* offsets = offsets_out ? offsets_out : I(W.offsets);
   int32_t* row_src = row_src_out ? row_src_out : I(W.row_src);
-  hipError_t e = moe::launch_route(*p, logits, idx, wts, nullptr, s);
+  // Five launches with the separate schedule, four with the fused ones:
+  // route + dispatch counts; scan + row-band plan + scatter; the expert
+  // GEMM(s), Linear-1 gathering its rows from X; the weighted combine.
+  float* xps = fp8 ? F(W.x_perm_scale) : nullptr;
+  hipError_t e = moe::launch_route_count(*p, L, logits, idx, wts, I(L.blk_counts), I(L.tok_cnt), I(W.meta), s);
   if (e == hipSuccess)
-    e = moe::launch_dispatch(*p, L, moe::dispatch_scratch(L, ws), X, X_scale, idx, wts, counts, offsets, row_src,
-                             I(W.row_dst), I(W.tok_off),
-                             F(W.comb_w), ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, s);
+    e = moe::launch_scan_plan_scatter(*p, L, ws, X_scale, idx, wts, counts, offsets, row_src, I(W.row_dst),
+                                      I(W.tok_off), F(W.comb_w), xps, s);
   if (e == hipSuccess)
-    e = moe::launch_expert_forward(*p, L, ws, ws + W.x_perm, fp8 ? F(W.x_perm_scale) : nullptr, offsets,
-                                   I(W.row_dst), W1, W1_scale, W2, W2_scale, ws + W.combine_buf, s, nullptr, 0,
-                                   true);
+    e = moe::launch_expert_forward_fused(*p, L, ws, X, row_src, xps, I(W.row_dst), W1, W1_scale, W2, W2_scale,
+                                         ws + W.combine_buf, s);
   if (e == hipSuccess) e = moe::launch_combine(*p, ws + W.combine_buf, I(W.tok_off), F(W.comb_w), Y, Y_fp32, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

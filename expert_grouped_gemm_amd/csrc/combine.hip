@@ -18,58 +18,12 @@ namespace moe {
 namespace {
 
 template <bool BF16_IN>
-__device__ __forceinline__ void load8(const void* buf, size_t row, int d, int c, float (&v)[8]) {
-  if constexpr (BF16_IN) {
-    const uint4 u = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(buf) + row * d)[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(buf) + row * d) + 2 * c;
-    const float4 a = src[0], b = src[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
-
-template <bool BF16_IN>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ buf,
                                                       const int32_t* __restrict__ tok_off,
                                                       const float* __restrict__ comb_w, int T, int d, int cap,
                                                       uint16_t* __restrict__ Y, float* __restrict__ Y32) {
-  const int vec = d >> 3;  // 8 columns per lane-step
-  for (int q = blockIdx.x; q < T; q += gridDim.x) {
-    const int p0 = tok_off[q], p1 = tok_off[q + 1];
-    const bool ok = 0 <= p0 && p0 <= p1 && p1 <= cap;
-    for (int c = threadIdx.x; c < vec; c += blockDim.x) {
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = ok ? 0.0f : __builtin_nanf("");
-      if (ok) {
-        for (int p = p0; p < p1; ++p) {
-          const float wgt = comb_w[p];
-          float v[8];
-          load8<BF16_IN>(buf, (size_t)p, d, c, v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
-        }
-      }
-      uint4 o;
-      o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-      o.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-      o.z = f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
-      o.w = f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
-      reinterpret_cast<uint4*>(Y + (size_t)q * d)[c] = o;
-      if (Y32) {
-        float4* dst = reinterpret_cast<float4*>(Y32 + (size_t)q * d) + 2 * c;
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      }
-    }
-  }
+  for (int q = blockIdx.x; q < T; q += gridDim.x)
+    combine_row<BF16_IN>(buf, tok_off, comb_w, q, d, cap, Y, Y32, threadIdx.x, blockDim.x);
 }
 
 }  // namespace

@@ -17,6 +17,7 @@
 //                running base per expert from LDS.
 //   4. gather  : X_perm[r] = X[row_src[r] / k], 16-byte lanes, coalesced.
 #include "moe_internal.h"
+#include "plan_device.h"
 
 namespace moe {
 namespace {
@@ -96,13 +97,10 @@ __device__ int block_exclusive_scan_1024(int v, int* sh, int* total) {
 // topk_idx that lists an expert twice for one token) sets the capacity error
 // bit and A = 0: the scatter then stores only what fits, the gather nothing,
 // and the expert GEMM's own check of the offsets stops it.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tok_cnt, int T, int El,
-                                                             int nblk, int cap,
-                                                             int32_t* __restrict__ blk_counts,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ tok_off,
-                                                             int32_t* __restrict__ meta) {
+__device__ __forceinline__ void scan_body(const int32_t* __restrict__ tok_cnt, int T, int El, int nblk, int cap,
+                                          int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
+                                          int32_t* __restrict__ offsets, int32_t* __restrict__ tok_off,
+                                          int32_t* __restrict__ meta) {
   __shared__ int sh[64];
   __shared__ int tot[1024];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -210,26 +208,32 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   if (threadIdx.x == 0) tok_off[T] = total;
 }
 
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ tok_cnt, int T, int El,
+                                                             int nblk, int cap, int32_t* __restrict__ blk_counts,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ tok_off,
+                                                             int32_t* __restrict__ meta) {
+  scan_body(tok_cnt, T, El, nblk, cap, blk_counts, counts, offsets, tok_off, meta);
+}
+
 // One wavefront per chunk, walking its assignments in order, 64 at a time.
 // A token's k experts are distinct, so within one expert the order is the
 // order of the tokens; the rank of a lane among the lanes of its group that
 // hold the same expert comes from a ballot (a match-any loop), the running
 // base of each expert (offset + chunk prefix) from LDS.
-__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
-                                                              const float* __restrict__ w, int T, int k, int S,
-                                                              int chunk, int e_begin, int El, int nblk, int cap,
-                                                              const int32_t* __restrict__ blk_prefix,
-                                                              const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ tok_off,
-                                                              int32_t* __restrict__ row_src,
-                                                              int32_t* __restrict__ row_dst,
-                                                              float* __restrict__ comb_w) {
-  extern __shared__ int32_t running[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < El; e += 64) running[e] = offsets[e] + blk_prefix[(size_t)e * nblk + blockIdx.x];
-  __syncthreads();
+// Chunk b of the assignments, walked by one wavefront (lane = 0..63) whose
+// running[] (El ints of LDS) already holds each expert's base for the chunk.
+// With X_scale set (the fused e4m3 path, where Linear-1 reads X itself), the
+// wavefront also writes the gathered row scales X_perm_scale[c * cap + pos].
+__device__ __forceinline__ void scatter_chunk(int b, int lane, int32_t* running, const int32_t* __restrict__ idx,
+                                              const float* __restrict__ w, int T, int k, int S, int chunk,
+                                              int e_begin, int El, int cap, const int32_t* __restrict__ tok_off,
+                                              int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
+                                              float* __restrict__ comb_w, const float* __restrict__ X_scale,
+                                              int dblocks, float* __restrict__ X_perm_scale) {
   const int Tk = T * k;
-  const int a0 = blockIdx.x * chunk;
+  const int a0 = b * chunk;
   const int a1 = min(Tk, a0 + chunk);
   int next = (a0 + lane < a1) ? idx[a0 + lane] : 0;
   for (int g = a0; g < a1; g += 64) {
@@ -260,8 +264,32 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
         row_dst[pos] = slot;
       }
       if (slot < cap) comb_w[slot] = w[a];
+      if (X_scale && pos < cap)
+        for (int c = 0; c < dblocks; ++c) X_perm_scale[(size_t)c * cap + pos] = X_scale[(size_t)(t >> 7) * dblocks + c];
     }
   }
+}
+
+// One wavefront per chunk, walking its assignments in order, 64 at a time.
+// A token's k experts are distinct, so within one expert the order is the
+// order of the tokens; the rank of a lane among the lanes of its group that
+// hold the same expert comes from a ballot (a match-any loop), the running
+// base of each expert (offset + chunk prefix) from LDS.
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ w, int T, int k, int S,
+                                                              int chunk, int e_begin, int El, int nblk, int cap,
+                                                              const int32_t* __restrict__ blk_prefix,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ tok_off,
+                                                              int32_t* __restrict__ row_src,
+                                                              int32_t* __restrict__ row_dst,
+                                                              float* __restrict__ comb_w) {
+  extern __shared__ int32_t running[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < El; e += 64) running[e] = offsets[e] + blk_prefix[(size_t)e * nblk + blockIdx.x];
+  __syncthreads();
+  scatter_chunk(blockIdx.x, lane, running, idx, w, T, k, S, chunk, e_begin, El, cap, tok_off, row_src, row_dst,
+                comb_w, nullptr, 0, nullptr);
 }
 
 // X_perm[r, :] = X[row_src[r] / k, :] for r < A; fp8 also gathers the row's
@@ -287,7 +315,131 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const uint8_t* __r
   }
 }
 
+struct FusedDispatch {
+  const int32_t* idx;
+  const float* w;
+  int T, k, S, chunk, e_begin, El, nblk, cap;
+  int32_t* blk_counts;
+  const int32_t* tok_cnt;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* tok_off;
+  int32_t* row_src;
+  int32_t* row_dst;
+  float* comb_w;
+  const float* X_scale;  // e4m3 activations: their block scales, gathered per row into X_perm_scale
+  int dblocks;
+  float* X_perm_scale;
+  int32_t* meta;
+  // the expert GEMM's planning step
+  int N1, G, wave_experts, sort_bands, Pmax, nblk_done;
+  int32_t* blk_done;
+  int32_t* band_expert;
+  int32_t* band_row0;
+  int32_t* band_rows;
+  int32_t* l2_full;
+  int32_t* wave_band0;
+};
+
+// moe_layer_forward's dispatch, one launch after the fused router: block 0
+// runs the scan (per-expert chunk bases, counts, offsets, tok_off), raises
+// meta[META_SCAN_DONE] with a device-scope release, then runs the expert
+// GEMM's planning step (row bands, readiness counters); every other block
+// waits for the flag (thread 0 polls, bounded; a timeout sets the error flag
+// and the block stores nothing), acquires, and scatters 16 chunks, one per
+// wavefront. Block 0 is dispatched first and waits for nothing, so the wait
+// always ends. The router kernel cleared the flag.
+__global__ __launch_bounds__(1024) void scan_plan_scatter_kernel(FusedDispatch F) {
+  if (blockIdx.x == 0) {
+    scan_body(F.tok_cnt, F.T, F.El, F.nblk, F.cap, F.blk_counts, F.counts, F.offsets, F.tok_off, F.meta);
+    __syncthreads();  // (a workgroup barrier also orders the block's global stores before thread 0's release)
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(F.meta + META_SCAN_DONE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the scatter blocks run while this block plans the row bands
+    plan_body(F.offsets, F.El, F.cap, F.N1, F.G, F.wave_experts, F.sort_bands, F.Pmax,
+              ARG_ERR_OFFSETS | ARG_ERR_ROW_DST, F.blk_done, F.nblk_done, F.band_expert, F.band_row0, F.band_rows,
+              F.l2_full, F.wave_band0, F.meta);
+    return;
+  }
+  __shared__ int ok;
+  if (threadIdx.x == 0) {
+    int spins = 0, good = 1;
+    while (__hip_atomic_load(F.meta + META_SCAN_DONE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(F.meta + META_ERR, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        good = 0;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    ok = good;
+  }
+  __syncthreads();
+  if (!ok) return;
+  extern __shared__ int32_t running_all[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = (blockIdx.x - 1) * 16 + w;
+  int32_t* running = running_all + w * F.El;
+  if (b < F.nblk)
+    for (int e = lane; e < F.El; e += 64) running[e] = F.offsets[e] + F.blk_counts[(size_t)e * F.nblk + b];
+  __syncthreads();
+  if (b < F.nblk)
+    scatter_chunk(b, lane, running, F.idx, F.w, F.T, F.k, F.S, F.chunk, F.e_begin, F.El, F.cap, F.tok_off,
+                  F.row_src, F.row_dst, F.comb_w, F.X_scale, F.dblocks, F.X_perm_scale);
+}
+
 }  // namespace
+
+hipError_t launch_scan_plan_scatter(const moe_problem_t& p, const Layout& L, char* ws, const float* X_scale,
+                                    const int32_t* idx, const float* w, int32_t* counts, int32_t* offsets,
+                                    int32_t* row_src, int32_t* row_dst, int32_t* tok_off, float* comb_w,
+                                    float* X_perm_scale, hipStream_t s) {
+  const int G = gemm_grid(p);
+  if (G <= 0) return hipErrorInvalidDevice;
+  const bool fp8 = p.dtype != MOE_DTYPE_BF16;
+  const TileChoice tc = choose_tiles(p, L, G);
+  FusedDispatch F{};
+  F.idx = idx;
+  F.w = w;
+  F.T = p.T;
+  F.k = p.k;
+  F.S = p.num_segments;
+  F.chunk = L.chunk;
+  F.e_begin = p.e_begin;
+  F.El = L.E_l;
+  F.nblk = L.nblk;
+  F.cap = L.cap;
+  F.blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+  F.tok_cnt = reinterpret_cast<const int32_t*>(ws + L.tok_cnt);
+  F.counts = counts;
+  F.offsets = offsets;
+  F.tok_off = tok_off;
+  F.row_src = row_src;
+  F.row_dst = row_dst;
+  F.comb_w = comb_w;
+  F.X_scale = fp8 ? X_scale : nullptr;
+  F.dblocks = p.d / 128;
+  F.X_perm_scale = fp8 ? X_perm_scale : nullptr;
+  F.meta = reinterpret_cast<int32_t*>(ws + L.pub.meta);
+  F.N1 = p.f / (32 * tc.nnb1);
+  F.G = G;
+  F.wave_experts = p.wave_experts;
+  F.sort_bands = resolve_schedule(p) == MOE_SCHED_EXPERT_WAVE ? 0 : 1;
+  F.Pmax = L.Pmax;
+  F.blk_done = reinterpret_cast<int32_t*>(ws + L.blk_done);
+  F.nblk_done = fp8 ? L.Pmax * (p.f / 128) : 0;
+  F.band_expert = reinterpret_cast<int32_t*>(ws + L.band_expert);
+  F.band_row0 = reinterpret_cast<int32_t*>(ws + L.band_row0);
+  F.band_rows = reinterpret_cast<int32_t*>(ws + L.band_rows);
+  F.l2_full = reinterpret_cast<int32_t*>(ws + L.l2_full);
+  F.wave_band0 = reinterpret_cast<int32_t*>(ws + L.wave_band0);
+  const int blocks = 1 + (L.nblk + 15) / 16;
+  hipLaunchKernelGGL(scan_plan_scatter_kernel, dim3(blocks), dim3(1024), 16 * L.E_l * 4, s, F);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const moe_problem_t& p, const Layout& L, const DispatchScratch& sc, const void* X,
                            const float* X_scale, const int32_t* idx, const float* w, int32_t* counts,

@@ -103,6 +103,10 @@ struct GemmParams {
   int32_t* row_done;      // or null: per 32-row block of output rows, output elements stored (Linear-2)
   int row_done_len;       // blocks row_done holds
   int c_bf16;             // the Linear-2 epilogue rounds its outputs to bf16 (MOE_FLAG_BF16_COMBINE_BUF)
+  // Linear-1 gathers its rows (moe_layer_forward): band row r is X row
+  // a_src[r] / a_k (X is then the token rows, not X_perm); null: X_perm rows
+  const int32_t* a_src;
+  int a_k;
 };
 
 // Launch the persistent expert-GEMM kernel of one operand type (bf16 in
@@ -149,6 +153,13 @@ struct Tile {
   const uint8_t* Eg;      // scale row of the first weight row of the first half
   const uint8_t* Eu;      // ... of the second half
   size_t epitch;          // bytes between consecutive scale rows
+  // Linear-1 with gathered rows: band row r is row a_src[r] / a_k of A
+  // (which then points at X); null: row row0 + r
+  const int32_t* a_src;
+  int a_k;
+  // the A rows this lane loads, one per band-row load instruction of a stage
+  // (filled at the start of the tile, once its row-block count is known)
+  int arow[4];
 };
 
 // Operand types of the expert GEMM (the template parameter OT): bf16
@@ -280,8 +291,7 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
     const bool part = REM && j == NAF;
     const int r0 = part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI;
     const int r = r0 + sub;
-    const int gr = r < t.rows ? r : t.rows - 1;  // rows past the band re-read its last row
-    const uint8_t* g = t.A + (size_t)gr * t.lda + kt * KB + ((slot ^ chunk_swizzle<KB>(r)) << 4);
+    const uint8_t* g = t.A + (size_t)t.arow[j] * t.lda + kt * KB + ((slot ^ chunk_swizzle<KB>(r)) << 4);
     if (!part || sub < RPW) __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
   } else if (j < NA + NBW) {
     const int sub = lane / CHB, slot = lane % CHB;
@@ -315,6 +325,26 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
       const float* g = lane == 0 ? t.Sg + kt : t.Su + kt;
       if (lane < 2) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4, 4, 0, 0);
     }
+  }
+}
+
+// The A (band) row each band-row load instruction j of this lane reads, as
+// issue_load lays the stage out: rows past the band re-read its last row;
+// with gathered rows, band row r is A row a_src[row0 + r] / a_k.
+template <int MB, int NNB, int OT>
+__device__ __forceinline__ void fill_arow(Tile& t, int tid) {
+  constexpr int KB = stage_k_bytes(OT), CH = KB / 16, RPI = 64 / CH;
+  constexpr int NW = gemm_threads(OT) / 64, ROUND = NW * RPI;
+  constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
+  static_assert(NA <= 4, "band-row load instructions per stage");
+  const int w = tid >> 6, sub = (tid & 63) / CH;
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    constexpr int RPW = REM / NW;
+    const bool part = REM && j == NAF;
+    const int r = (part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI) + sub;
+    const int gr = r < t.rows ? r : t.rows - 1;
+    t.arow[j] = t.a_src ? t.a_src[t.row0 + gr] / t.a_k : t.row0 + gr;
   }
 }
 
@@ -582,9 +612,11 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
 template <int MB, int NMB, int NNB, bool L1, int OT>
-__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, lds_t* lds, uint64_t& t_main) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
+  Tile t = t0;
+  fill_arow<MB, NNB, OT>(t, tid);
   constexpr int S = ring_stages(MB, NNB, OT), SB = stage_bytes(MB, NNB, OT), LD = stage_loads(MB, NNB, OT);
   static_assert(S >= 2, "the LDS ring needs two stages");
   f32x16 acc[NMB > 0 ? NMB : 1][WaveGrid<NNB, OT>::NCB];
@@ -865,7 +897,9 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
     const int bn = nnb * 32;  // SwiGLU columns: bn gate rows and bn up rows
     t.lda = (size_t)P.d * esz;
     t.ldb = W4 ? (size_t)P.d / 2 : (size_t)P.d * esz;
-    t.A = P.X + (size_t)t.row0 * t.lda;
+    t.A = P.X;  // rows by t.arow: X_perm row row0 + r, or X row a_src[row0 + r] / k
+    t.a_src = P.a_src;
+    t.a_k = P.a_k;
     const uint8_t* We = P.W1 + (size_t)e * 2 * P.f * t.ldb;
     t.Bg = We + (size_t)(n * bn) * t.ldb;
     t.Bu = We + (size_t)(P.f + n * bn) * t.ldb;
@@ -887,7 +921,9 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
     const int bn = nnb * 64;  // output columns
     t.lda = (size_t)P.f * esz;
     t.ldb = W4 ? (size_t)P.f / 2 : (size_t)P.f * esz;
-    t.A = P.H + (size_t)t.row0 * t.lda;
+    t.A = P.H;
+    t.a_src = nullptr;
+    t.a_k = 1;
     t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * bn) * t.ldb;
     t.Bu = t.Bg + (size_t)(bn / 2) * t.ldb;
     t.ktiles = P.f * esz / stage_k_bytes(OT);

@@ -23,7 +23,12 @@ constexpr int gemm_threads(bool) { return 512; }
 constexpr int kGemmLds = 160 * 1024;  // the whole LDS of a CU: one persistent workgroup per CU
 
 constexpr int kMetaInts = 64;
-enum MetaSlot { META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4, META_ARG_ERR = 5 };
+enum MetaSlot {
+  META_A = 0, META_P = 1, META_ERR = 2, META_NWAVES = 3, META_TRACE_N = 4, META_ARG_ERR = 5,
+  // moe_layer_forward's fused dispatch kernel: the scan-done flag, cleared by
+  // the router kernel that starts each call
+  META_SCAN_DONE = 6
+};
 // Bits of meta[META_ARG_ERR]: device-side checks of arguments the host cannot
 // see (they live in device memory). A call that uses a workspace clears the
 // whole word when it starts (the workspace may hold anything before its first
@@ -53,16 +58,17 @@ struct Layout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Dispatch chunk size: a multiple of 64 assignments (one wavefront step),
-// as small as possible while the [chunks, E_l] count matrix keeps at most 512
-// chunks and 2^20 entries.
-inline int dispatch_chunk(int64_t Tk, int El) {
+// Dispatch chunk size in assignments: a whole number of tokens (k
+// assignments each, so the fused router can count a chunk's tokens), at
+// least 64 (one wavefront step), as small as possible while the [chunks, E_l]
+// count matrix keeps at most 512 chunks and 2^20 entries.
+inline int dispatch_chunk(int64_t Tk, int El, int k) {
   int64_t nmax = (1 << 20) / (El > 0 ? El : 1);
   if (nmax > 512) nmax = 512;
   if (nmax < 1) nmax = 1;
   int64_t per = (Tk + nmax - 1) / nmax;
-  per = (per + 63) / 64 * 64;
   if (per < 64) per = 64;
+  per = (per + k - 1) / k * k;
   return (int)per;
 }
 
@@ -82,7 +88,7 @@ inline Layout make_layout(const moe_problem_t& p) {
   const size_t esz = fp8 ? 1 : 2;
   L.cap = (int)cap;
   L.E_l = El;
-  L.chunk = dispatch_chunk((int64_t)p.T * p.k, El);
+  L.chunk = dispatch_chunk((int64_t)p.T * p.k, El, p.k);
   L.nblk = (int)(((int64_t)p.T * p.k + L.chunk - 1) / L.chunk);
   L.Pmax = (int)((cap + kBM - 1) / kBM) + El;
   size_t o = 0;
@@ -149,6 +155,20 @@ hipError_t launch_expert_forward(const moe_problem_t& p, const Layout& L, char* 
 hipError_t launch_combine(const moe_problem_t& p, const void* combine_buf, const int32_t* tok_off,
                           const float* comb_w, void* Y, float* Y_fp32, hipStream_t s);
 
+// moe_layer_forward's fused launches (route and dispatch counts; scan, band
+// plan and scatter; the expert GEMMs with Linear-1 gathering its rows from X;
+// then the combine kernel).
+hipError_t launch_route_count(const moe_problem_t& p, const Layout& L, const float* logits, int32_t* idx, float* w,
+                              int32_t* blk_counts, int32_t* tok_cnt, int32_t* meta, hipStream_t s);
+hipError_t launch_scan_plan_scatter(const moe_problem_t& p, const Layout& L, char* ws, const float* X_scale,
+                                    const int32_t* idx, const float* w, int32_t* counts, int32_t* offsets,
+                                    int32_t* row_src, int32_t* row_dst, int32_t* tok_off, float* comb_w,
+                                    float* X_perm_scale, hipStream_t s);
+hipError_t launch_expert_forward_fused(const moe_problem_t& p, const Layout& L, char* ws, const void* X,
+                                       const int32_t* row_src, const float* X_perm_scale, const int32_t* row_dst,
+                                       const void* W1, const void* W1_scale, const void* W2, const void* W2_scale,
+                                       void* combine_buf, hipStream_t s);
+
 // Owner-aligned return path (validated arguments; see moe_owner_plan,
 // moe_owner_gather and moe_segment_copy).
 struct OwnerPlanSizes {
@@ -193,6 +213,63 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Eight consecutive columns (8 c .. 8 c + 7) of combine-buffer row p as fp32.
+template <bool BF16_IN>
+__device__ __forceinline__ void combine_load8(const void* buf, size_t p, int d, int c, float (&v)[8]) {
+  if constexpr (BF16_IN) {
+    const uint4 u = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(buf) + p * d)[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(buf) + p * d) + 2 * c;
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// The weighted combine of output row q (Cui et al., Section 2.1 step (5)):
+// Y[q] = sum over slots p in [tok_off[q], tok_off[q+1]) of comb_w[p] *
+// buf[p], ascending p, fp32 fused multiply-add, rounded once to bf16 (and
+// the fp32 sums to Y32 if set). Threads tid, tid + nthr, ... take 8 columns
+// each. A slot range outside [0, cap) gives a NaN row and reads nothing.
+template <bool BF16_IN>
+__device__ __forceinline__ void combine_row(const void* buf, const int32_t* tok_off, const float* comb_w, int q,
+                                            int d, int cap, uint16_t* Y, float* Y32, int tid, int nthr) {
+  const int vec = d >> 3;
+  const int p0 = tok_off[q], p1 = tok_off[q + 1];
+  const bool ok = 0 <= p0 && p0 <= p1 && p1 <= cap;
+  for (int c = tid; c < vec; c += nthr) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = ok ? 0.0f : __builtin_nanf("");
+    if (ok) {
+      for (int p = p0; p < p1; ++p) {
+        const float wgt = comb_w[p];
+        float v[8];
+        combine_load8<BF16_IN>(buf, (size_t)p, d, c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
+    reinterpret_cast<uint4*>(Y + (size_t)q * d)[c] = o;
+    if (Y32) {
+      float4* dst = reinterpret_cast<float4*>(Y32 + (size_t)q * d) + 2 * c;
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
 
 // Output row of token t with S destination segments.
 __host__ __device__ __forceinline__ int y_row_of_token(int t, int T, int S) {

@@ -20,6 +20,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
+constexpr int kRouteCountWaves = 8;  // wavefronts of the fused router's per-chunk block
 
 template <int CTRL>
 __device__ __forceinline__ int dpp(int x) {
@@ -50,16 +51,11 @@ __device__ __forceinline__ int wave_min_i32(int x) {
              min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
+// Route token row `row` (E logits) with the whole wavefront: lane j < k
+// ends with slot j's expert (*my_e) and gate weight (*my_w).
 template <int PER>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w,
-                                                         int32_t* __restrict__ counts_global) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wavefronts: the DPP reductions need every lane
-  const float* row = logits + (size_t)t * E;
-
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane, int& my_e,
+                                            float& my_w) {
   // PER = ceil(E / 64) logits per lane (1, 2, 4, 8 or 16): the selection
   // scans only the slots that exist
   float v[PER];
@@ -72,7 +68,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if (!present) taken |= 1u << i;
   }
 
-  int my_e = -1;  // lane j keeps slot j's expert and logit
+  my_e = -1;  // lane j keeps slot j's expert and logit
   float my_v = 0.0f;
   for (int j = 0; j < k; ++j) {
     float best = -__builtin_huge_valf();
@@ -97,11 +93,67 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const float ex = (lane < k) ? expf(my_v - m) : 0.0f;
   float sum = 0.0f;
   for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  my_w = ex / sum;
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w,
+                                                         int32_t* __restrict__ counts_global) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wavefronts: the DPP reductions need every lane
+  int my_e;
+  float my_w;
+  route_token<PER>(logits + (size_t)t * E, E, k, lane, my_e, my_w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_e;
-    topk_w[(size_t)t * k + lane] = ex / sum;
+    topk_w[(size_t)t * k + lane] = my_w;
     if (counts_global) atomicAdd(&counts_global[my_e], 1);
   }
+}
+
+// moe_layer_forward's first launch: routing fused with the dispatch's count.
+// Block b routes the tokens of dispatch chunk b (chunk / k tokens, one
+// wavefront per token in turn) and counts their local assignments per
+// expert in LDS (blk_counts[e][b]) and per output row (tok_cnt[q(t)]), as the
+// dispatch's count kernel does from topk_idx. Block 0 also starts the call's
+// device-side state: the error words and the next launch's scan-done flag.
+template <int PER>
+__global__ __launch_bounds__(512) void route_count_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int S, int chunk_tok, int e_begin, int El, int nblk,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w,
+                                                          int32_t* __restrict__ blk_counts,
+                                                          int32_t* __restrict__ tok_cnt,
+                                                          int32_t* __restrict__ meta) {
+  extern __shared__ int32_t hist[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) {
+    meta[META_ERR] = 0;
+    meta[META_ARG_ERR] = 0;
+    meta[META_SCAN_DONE] = 0;
+  }
+  for (int e = threadIdx.x; e < El; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t0 = b * chunk_tok, t1 = min(T, t0 + chunk_tok);
+  for (int t = t0 + w; t < t1; t += kRouteCountWaves) {
+    int my_e;
+    float my_w;
+    route_token<PER>(logits + (size_t)t * E, E, k, lane, my_e, my_w);
+    const bool local = lane < k && (unsigned)(my_e - e_begin) < (unsigned)El;
+    if (lane < k) {
+      topk_idx[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = my_w;
+    }
+    if (local) atomicAdd(&hist[my_e - e_begin], 1);
+    const int c = __popcll(__ballot(local));
+    if (lane == 0) tok_cnt[y_row_of_token(t, T, S)] = c;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += blockDim.x) blk_counts[(size_t)e * nblk + b] = hist[e];
 }
 
 __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
@@ -109,6 +161,22 @@ __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
 }
 
 }  // namespace
+
+hipError_t launch_route_count(const moe_problem_t& p, const Layout& L, const float* logits, int32_t* idx, float* w,
+                              int32_t* blk_counts, int32_t* tok_cnt, int32_t* meta, hipStream_t s) {
+  const int per = (p.E_global + 63) >> 6;  // E_global <= 1024 (validated)
+  const int chunk_tok = L.chunk / p.k;      // the dispatch chunk is a whole number of tokens
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(L.nblk), dim3(64 * kRouteCountWaves), L.E_l * 4, s, logits, p.T, p.E_global, p.k,
+                       p.num_segments, chunk_tok, p.e_begin, L.E_l, L.nblk, idx, w, blk_counts, tok_cnt, meta);
+  };
+  if (per <= 1) go(route_count_kernel<1>);
+  else if (per <= 2) go(route_count_kernel<2>);
+  else if (per <= 4) go(route_count_kernel<4>);
+  else if (per <= 8) go(route_count_kernel<8>);
+  else go(route_count_kernel<16>);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const moe_problem_t& p, const float* logits, int32_t* idx, float* w,
                         int32_t* counts_global, hipStream_t s) {

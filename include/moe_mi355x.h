@@ -171,7 +171,8 @@ typedef struct moe_problem {
 /* Byte offsets of the intermediates inside a workspace (for inspection by
  * tests and callers). cap = the row capacity: T * min(k, E_l), or
  * p->row_capacity if set. moe_layer_forward writes every region except one
- * whose output the caller passes in its place. */
+ * whose output the caller passes in its place, and x_perm (its Linear-1
+ * reads each row band's X rows where they are). */
 typedef struct moe_workspace_layout {
   size_t topk_idx;      /* int32 [T, k]                                     */
   size_t topk_w;        /* fp32  [T, k]                                     */
@@ -277,7 +278,12 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf
  * Section 2.2 "MegaMoE Execution" (Dispatch, Linear-1, activation, Linear-2,
  * Combine): route -> dispatch -> grouped Linear-1 + SwiGLU -> grouped
  * Linear-2 -> combine on one stream, with row counts kept on the device (no
- * host synchronisation). Inputs as for the component calls; Y bf16 [T, d]
+ * host synchronisation), in five launches (four with the expert-wave or
+ * interleaved schedule): the router with the dispatch's counts; the scan,
+ * the expert GEMM's row-band plan and the scatter; the grouped GEMM(s), whose
+ * Linear-1 gathers each band's rows from X through row_src instead of a
+ * permuted copy; the weighted combine. The results are those of the
+ * component calls, bit for bit. Inputs as for the component calls; Y bf16 [T, d]
  * (segment-major with S > 1); Y_fp32 [T, d] or NULL (see
  * MOE_FLAG_FP32_Y_DEBUG). The optional outputs, each DEVICE memory or NULL,
  * receive the routing and dispatch results: topk_idx_out int32 [T, k],
@@ -285,7 +291,8 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const void* combine_buf
  * [E_l + 1], row_src_out int32 [cap] (rows >= A untouched). A non-NULL output
  * is written in place of its workspace region, which the call then leaves
  * unwritten. Every other intermediate is left in the workspace at
- * moe_workspace_get_layout's offsets. */
+ * moe_workspace_get_layout's offsets, except x_perm, which is not formed
+ * (x_perm_scale is: the e4m3 path's Linear-1 reads the row scales from it). */
 MOE_API moe_status_t moe_layer_forward(const moe_problem_t* p, const void* X, const float* X_scale,
                                        const float* logits, const void* W1, const void* W1_scale,
                                        const void* W2, const void* W2_scale, void* Y, float* Y_fp32,

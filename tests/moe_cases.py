@@ -42,6 +42,18 @@ def run_layer(p: moe.Problem, g, ws=None, want_fp32=True):
     return Y, Y32, ws
 
 
+def fill_x_perm(p: moe.Problem, g, ws):
+    """moe_layer_forward gathers Linear-1's rows from X and leaves the
+    workspace's x_perm unwritten; this runs moe_dispatch on the call's own
+    routing into the same workspace, which rewrites the dispatch results
+    (bit-identical) and fills x_perm (and x_perm_scale)."""
+    v = moe.workspace_views(p, ws)
+    moe.dispatch(p, g["X"], g.get("X_scale"), v["topk_idx"], v["topk_w"], v["counts"], v["offsets"], v["row_src"],
+                 v["row_dst"], v["tok_off"], v["comb_w"], v["x_perm"], v.get("x_perm_scale"), ws)
+    torch.cuda.synchronize()
+    return v
+
+
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
     ax = np.abs(x)
     e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))

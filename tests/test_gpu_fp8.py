@@ -12,7 +12,7 @@ import torch
 
 import moe_synth
 import oracle
-from moe_cases import check_y, problem_of, run_layer, to_gpu
+from moe_cases import check_y, fill_x_perm, problem_of, run_layer, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,8 @@ def test_fp8_dispatch_codes_and_scales_exact(name):
     inp, g, p, Y, Y32, ws = _run(cfg)
     ref = oracle.moe_layer(inp, cfg)
     v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items()}
+    fused_scale = v["x_perm_scale"].clone()       # written by the fused call's scatter
+    v["x_perm"] = fill_x_perm(p, g, ws)["x_perm"].cpu()
     A = ref["A"]
     np.testing.assert_array_equal(v["topk_idx"].numpy(), ref["topk_idx"])
     np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
@@ -50,6 +52,7 @@ def test_fp8_dispatch_codes_and_scales_exact(name):
     np.testing.assert_array_equal(v["x_perm"].numpy()[:A], inp["X"].numpy()[tok])
     xs = inp["X_scale"].numpy()
     np.testing.assert_array_equal(v["x_perm_scale"].numpy()[:, :A], xs[tok // 128].T)
+    np.testing.assert_array_equal(fused_scale.numpy()[:, :A], xs[tok // 128].T)
 
 
 @pytest.mark.parametrize("tiles", ["narrow", "wide"])

@@ -22,7 +22,7 @@ import torch
 
 import moe_synth
 import oracle
-from moe_cases import check_y, problem_of, run_layer
+from moe_cases import check_y, fill_x_perm, problem_of, run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +106,8 @@ def test_full_size_parity(name, sched):
         assert stats["rel_fro_vs_fp32_h"] <= 3e-2, stats
     print(f"[fullsize] {name}/{sched}: {stats}", flush=True)
 
-    # gathered X rows of the sampled bands are exact copies
-    xp = moe.workspace_views(p, ws)["x_perm"]
+    # the component dispatch's gathered X rows of the sampled bands are exact copies
+    xp = fill_x_perm(p, g, ws)["x_perm"]
     got = xp[torch.as_tensor(sampled_rows, device="cuda")].cpu()
     want = g["X"][torch.as_tensor(disp["row_src"][sampled_rows] // cfg.k, device="cuda")].cpu()
     assert torch.equal(got.view(torch.uint8), want.view(torch.uint8))

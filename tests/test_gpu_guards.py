@@ -17,7 +17,7 @@ import torch
 import expert_grouped_gemm_amd as moe
 import moe_synth
 import oracle
-from moe_cases import check_y, problem_of, run_layer, to_gpu
+from moe_cases import check_y, fill_x_perm, problem_of, run_layer, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_offsets_past_capacity_store_nothing(sched):
     p = problem_of(CFG, sched=sched)
     cap = moe.row_capacity(p)
     _, _, ws = run_layer(p, g)                      # a good call first: the workspace holds real values
-    v = moe.workspace_views(p, ws)
+    v = fill_x_perm(p, g, ws)
     x_perm = v["x_perm"].clone()
     row_dst = v["row_dst"].clone()
     h_before = v["h"].clone()
@@ -67,7 +67,7 @@ def test_row_dst_outside_capacity_is_not_stored():
     p = problem_of(CFG, sched="separate")
     cap = moe.row_capacity(p)
     _, _, ws = run_layer(p, g)
-    v = moe.workspace_views(p, ws)
+    v = fill_x_perm(p, g, ws)
     A = int(v["meta"][0])
     row_dst = v["row_dst"].clone()
     bad_rows = [0, A // 2, A - 1]

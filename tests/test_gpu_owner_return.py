@@ -16,7 +16,7 @@ import torch
 import expert_grouped_gemm_amd as moe
 import moe_synth
 import oracle
-from moe_cases import problem_of, run_layer, to_gpu
+from moe_cases import fill_x_perm, problem_of, run_layer, to_gpu
 from oracle import owner_layout as ol
 
 pytestmark = pytest.mark.gpu
@@ -283,7 +283,7 @@ def test_signal_counts_every_output_element(sched):
     g = to_gpu(moe_synth.generate(cfg))
     p = problem_of(cfg, sched=sched)
     _, _, ws = run_layer(p, g)
-    v = moe.workspace_views(p, ws)
+    v = fill_x_perm(p, g, ws)
     A = int(v["meta"][0].item())
     R = A
     iota = torch.arange(max(R, 1), dtype=torch.int32, device="cuda")

@@ -10,7 +10,7 @@ import torch
 
 import moe_synth
 import oracle
-from moe_cases import check_y, problem_of, run_layer, to_gpu
+from moe_cases import check_y, fill_x_perm, problem_of, run_layer, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,8 @@ def test_route_and_dispatch_bit_exact(name):
     np.testing.assert_array_equal(v["row_dst"].numpy()[:A], ref["row_dst"])
     np.testing.assert_array_equal(v["tok_off"].numpy(), ref["tok_off"])
     np.testing.assert_allclose(v["comb_w"].numpy()[:A], ref["comb_w"], rtol=2e-6, atol=1e-7)
+    # the gathered rows of the component dispatch (the fused call reads X directly)
+    v["x_perm"] = fill_x_perm(p, to_gpu(inp), ws)["x_perm"].cpu()
     xs = inp["X"].view(torch.int16).numpy()
     np.testing.assert_array_equal(v["x_perm"].view(torch.int16).numpy()[:A], xs[ref["row_src"] // cfg.k])
 

@@ -81,7 +81,7 @@ def gemm_bytes(cfg, counts) -> float:
     return float(w + rows)
 
 
-GEMM_SOURCES = ("gemm_device.h", "gemm.hip", "gemm_bf16.hip", "gemm_fp8.hip")
+GEMM_SOURCES = ("gemm_device.h", "plan_device.h", "gemm.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_w4a8.hip")
 
 
 def gemm_source_digest():
@@ -318,7 +318,7 @@ def main():
                               "combine": round(comb_bytes / (stage_proto["combine"]["median_us"] * 1e-6) / 1e9
                                                / HBM_PEAK_GBPS, 4)},
             note="moe_dispatch and moe_combine each timed alone, 20 trials after one warm-up call, a 512 MiB "
-                 "write before every trial flushing the 256 MiB last-level cache; copy_GBps is a device-to-device "
+                 "read before every trial evicting the 256 MiB last-level cache; copy_GBps is a device-to-device "
                  "copy of the combine's byte count under the same protocol (the achievable streaming rate)"),
         "roofline": {
             "kernel": "moe_gemm_kernel (grouped Linear-1+SwiGLU+Linear-2, one persistent launch)"
@@ -509,13 +509,16 @@ def owner_return_summary(moe, cfg, args, g, v, gemm_std_us, A):
 
 def stage_protocol(moe, cfg, p, g, v, ws, Y, stream, trials=20):
     """moe_dispatch and moe_combine timed standalone: one warm-up call, then
-    `trials` trials each preceded by a 512 MiB write that flushes the 256 MiB
+    `trials` trials each preceded by a 512 MiB read that evicts the 256 MiB
     last-level cache, HIP events on the launch stream around the call alone;
     median, p10 and p90 in microseconds. A device-to-device copy of the
-    combine's algorithmic byte count (read + write) is timed the same way."""
+    combine's algorithmic byte count (read + write) is timed the same way.
+    The flush reads rather than writes: a written flush leaves up to 256 MiB
+    of dirty lines whose write-back then lands inside the timed call (it
+    slowed the same copy by about 45%)."""
     import numpy as np
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     esz = 1 if cfg.dtype != "bf16" else 2
     A = int(v["offsets"][-1])
     comb_bytes = A * cfg.d * 4 + cfg.T * cfg.d * 2
@@ -534,7 +537,7 @@ def stage_protocol(moe, cfg, p, g, v, ws, Y, stream, trials=20):
         fn()
         us = []
         for _ in range(trials):
-            flush.fill_(1)
+            flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()

@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--tiles", default="auto", choices=["auto", "narrow", "wide"],
                     help="expert-GEMM tile width (default: chosen from the shape)")
     ap.add_argument("--band-major", action="store_true", help="no grouped raster of the GEMM tile lists")
+    ap.add_argument("--bf16-combine-buf", action="store_true",
+                    help="MOE_FLAG_BF16_COMBINE_BUF: the token-ordered combine buffer in bf16 instead of fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace", action="store_true",
                     help="after the timed steps, run one call with per-tile timing and summarise the spans")
@@ -67,17 +69,17 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_bytes(cfg, counts) -> float:
+def gemm_bytes(cfg, counts, cbuf_esz=4) -> float:
     """Algorithmic HBM bytes of one grouped-GEMM launch (Linear-1 + SwiGLU +
     Linear-2): each local expert with at least one row streams its W1 and W2
-    once; per row: X_perm read (d), H write and read (2f), combine-buffer
-    write (4d bytes)."""
+    once; per row: X row read (d), H write and read (2f), combine-buffer
+    write (d elements of cbuf_esz bytes: 4, or 2 with the bf16 buffer)."""
     esz = 1 if cfg.dtype != "bf16" else 2              # activations (e4m3 for fp8 and W4A8)
     wesz = 0.5 + 1.0 / 32 if cfg.dtype == "w4a8_mxfp4" else esz   # MXFP4: 4-bit codes + an E8M0 byte per 32
     active = sum(1 for c in counts if c > 0)
     A = sum(counts)
     w = active * 3 * cfg.f * cfg.d * wesz
-    rows = A * (cfg.d * esz + 2 * cfg.f * esz + 4 * cfg.d)
+    rows = A * (cfg.d * esz + 2 * cfg.f * esz + cbuf_esz * cfg.d)
     return float(w + rows)
 
 
@@ -94,11 +96,13 @@ def gemm_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg, sched, tiles="auto", band_major=False):
+def measured_traffic(cfg, sched, tiles="auto", variant=False):
     """HBM bytes per grouped-GEMM launch measured with rocprofv3 FETCH_SIZE /
     WRITE_SIZE (scaled by a plain-copy calibration) for this workload and
     schedule, as recorded in profiles/gemm_traffic_<workload>_<sched>.md; null
-    when no record exists or the GEMM source changed since it was taken."""
+    when no record exists, the GEMM source changed since it was taken, or the
+    run is a variant the record does not cover (band-major order, bf16
+    combine buffer)."""
     path = os.path.join(ROOT, "profiles", f"gemm_traffic_{cfg.name}_{sched}.md")
     if not os.path.exists(path):
         return None
@@ -108,7 +112,7 @@ def measured_traffic(cfg, sched, tiles="auto", band_major=False):
         blob = json.loads(text.split("```json")[1].split("```")[0])
     except (IndexError, ValueError):
         return None
-    if blob.get("gemm_source_sha256_16") != digest or blob.get("tiles", "auto") != tiles or band_major:
+    if blob.get("gemm_source_sha256_16") != digest or blob.get("tiles", "auto") != tiles or variant:
         return None
     return blob.get("hbm_bytes_per_launch")
 
@@ -176,7 +180,9 @@ def main():
     torch.cuda.synchronize()
     p = moe.make_problem(cfg.T, cfg.d, cfg.f, cfg.E_global, cfg.k, cfg.e_begin, cfg.e_end, dtype=cfg.dtype,
                          num_segments=cfg.num_segments, sched=args.sched, lead_D=args.lead_D,
-                         quant_block=cfg.quant_block, tiles=args.tiles, band_major=args.band_major)
+                         quant_block=cfg.quant_block, tiles=args.tiles, band_major=args.band_major,
+                         bf16_combine_buf=args.bf16_combine_buf)
+    cbuf_esz = 2 if args.bf16_combine_buf else 4
     ws = moe.alloc_workspace(p)
     v = moe.workspace_views(p, ws)
     Y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
@@ -272,7 +278,7 @@ def main():
     peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
 
     esz = 1 if fp8 else 2
-    gb = gemm_bytes(cfg, counts)
+    gb = gemm_bytes(cfg, counts, cbuf_esz)
     gemm_us = gemm_call_us
     # The grouped GEMM is bound by HBM when its arithmetic intensity (useful
     # FLOP per algorithmic byte) is below the ridge point peak_flops / 8 TB/s.
@@ -283,7 +289,7 @@ def main():
     else:
         bound, achieved, rpeak, runit = "mfma", useful_flop / (gemm_us * 1e-6) / 1e12, peak, "TFLOP/s"
     disp_bytes = 2.0 * A * cfg.d * esz + cfg.T * cfg.k * 8.0
-    comb_bytes = A * cfg.d * 4.0 + cfg.T * cfg.d * 2.0
+    comb_bytes = A * cfg.d * float(cbuf_esz) + cfg.T * cfg.d * 2.0
     out = {
         "metric": "fused MoE-layer useful TFLOP/s (6*A*d*f per step); % of MFMA peak; dispatch/combine GB/s",
         "value": round(tflops, 2),
@@ -300,7 +306,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E_global": cfg.E_global,
                    "k": cfg.k, "local_experts": [cfg.e_begin, cfg.e_end], "segments": cfg.num_segments,
                    "sched": args.sched, "sched_run": moe.schedule_of(p), "tiles": args.tiles,
-                   "band_major": args.band_major,
+                   "band_major": args.band_major, "bf16_combine_buf": args.bf16_combine_buf,
                    "A_local_assignments": A, "parallelism": "single GPU (one EP share)"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "component_calls_ms_per_step": round(chain_ms, 4),
@@ -328,7 +334,7 @@ def main():
             "peak": rpeak,
             "unit": runit,
             "frac": round(achieved / rpeak, 4),
-            "traffic": measured_traffic(cfg, moe.schedule_of(p), args.tiles, args.band_major),
+            "traffic": measured_traffic(cfg, moe.schedule_of(p), args.tiles, args.band_major or args.bf16_combine_buf),
             "algorithmic_bytes_per_launch": gb,
             "useful_flop_per_launch": useful_flop,
             "arithmetic_intensity_flop_per_byte": round(intensity, 1),
@@ -521,7 +527,7 @@ def stage_protocol(moe, cfg, p, g, v, ws, Y, stream, trials=20):
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     esz = 1 if cfg.dtype != "bf16" else 2
     A = int(v["offsets"][-1])
-    comb_bytes = A * cfg.d * 4 + cfg.T * cfg.d * 2
+    comb_bytes = A * cfg.d * (2 if p.flags & moe.FLAG_BF16_COMBINE_BUF else 4) + cfg.T * cfg.d * 2
     half = comb_bytes // 2 // 16 * 16
     src = torch.empty(half, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)

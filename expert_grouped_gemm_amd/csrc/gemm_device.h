@@ -159,7 +159,7 @@ struct Tile {
   int a_k;
   // the A rows this lane loads, one per band-row load instruction of a stage
   // (filled at the start of the tile, once its row-block count is known)
-  int arow[4];
+  int arow[8];
 };
 
 // Operand types of the expert GEMM (the template parameter OT): bf16
@@ -196,15 +196,29 @@ __host__ __device__ constexpr int stage_bytes(int MB, int NNB, int OT) {
 __host__ __device__ constexpr int ring_stages(int MB, int NNB, int OT) {
   return kGemmLds / stage_bytes(MB, NNB, OT) > 8 ? 8 : kGemmLds / stage_bytes(MB, NNB, OT);
 }
-// global -> LDS loads issued per lane per stage (16 bytes each, plus one
-// 4-byte row-scale load with fp8)
+// Wavefronts that issue the ring's global -> LDS loads. The CU accepts about
+// one such 1 KiB instruction per 22 cycles, so a 64 KiB stage takes about
+// 1400 cycles to issue, and a wavefront blocked at an issue runs no MFMA.
+// bf16: one wavefront per SIMD (the last four) issues the whole stage, after
+// the step's barrier, while the other wavefront of its SIMD already runs its
+// MFMAs. With every wavefront issuing its share before the barrier, the
+// issue and the MFMAs ran one after the other: per-phase cycle counts of
+// the Mixtral Linear-1 K loop gave 17-33% of each step to issuing and 12-20%
+// to the barrier behind it, against 1.5% waiting for data. The fp8 and
+// MXFP4 kernels, whose wavefronts use the whole register file, keep every
+// wavefront issuing (the loaders' extra row registers would spill).
+__host__ __device__ constexpr int loader_waves(int OT) { return OT == OT_BF16 ? 4 : gemm_threads(OT) / 64; }
+__host__ __device__ constexpr bool split_loads(int OT) { return loader_waves(OT) < gemm_threads(OT) / 64; }
+
+// global -> LDS loads issued per loader lane per stage (16 bytes each, plus
+// one 4-byte row-scale load with fp8)
 // (band rows: a whole number of instructions per wavefront plus, when they
 // do not divide evenly, one partial instruction in every wavefront)
 __host__ __device__ constexpr int stage_a_rows_per_round(int OT) {
-  return gemm_threads(OT) * 16 / stage_k_bytes(OT);
+  return loader_waves(OT) * 64 * 16 / stage_k_bytes(OT);
 }
 __host__ __device__ constexpr int stage_b_rows_per_round(int OT) {
-  return gemm_threads(OT) * 16 / stage_kb_bytes(OT);
+  return loader_waves(OT) * 64 * 16 / stage_kb_bytes(OT);
 }
 __host__ __device__ constexpr int stage_loads(int MB, int NNB, int OT) {
   return (MB * 32 + stage_a_rows_per_round(OT) - 1) / stage_a_rows_per_round(OT) +
@@ -268,13 +282,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // first the band rows, then the weight rows, then the scales. Lane i of a
 // 16-byte instruction lands at LDS base + 16*i (64/CH rows of KB bytes, CH =
 // KB/16 chunks per row), lane i of a 4-byte instruction at base + 4*i.
-// issue_load issues instruction j of the stage. (Spreading a stage's loads
-// between the MFMAs of the previous stage, instead of issuing them together,
-// was measured no faster.)
+// issue_load issues instruction j of the stage; only the loader wavefronts
+// call it (w below is the loader index).
 template <int MB, int NNB, int OT>
 __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
   constexpr int KB = stage_k_bytes(OT), CH = KB / 16, RPI = 64 / CH;
-  constexpr int NW = gemm_threads(OT) / 64, ROUND = NW * RPI;
+  constexpr int NW = loader_waves(OT), ROUND = NW * RPI;
   static_assert(ROUND == stage_a_rows_per_round(OT), "rows per load round");
   // weight rows: KBB bytes each (64 for MXFP4), RPIB rows per instruction
   constexpr int KBB = stage_kb_bytes(OT), CHB = KBB / 16, RPIB = 64 / CHB, ROUNDB = NW * RPIB;
@@ -284,7 +297,7 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
   constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
   constexpr int NBW = NNB * 64 / ROUNDB, half = NNB * 32;
   static_assert(NBW * ROUNDB == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = (tid >> 6) - (gemm_threads(OT) / 64 - NW), lane = tid & 63;
   if (j < NA) {
     constexpr int RPW = REM / NW;  // rows per wavefront in the partial round
     const int sub = lane / CH, slot = lane % CH;
@@ -334,10 +347,11 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
 template <int MB, int NNB, int OT>
 __device__ __forceinline__ void fill_arow(Tile& t, int tid) {
   constexpr int KB = stage_k_bytes(OT), CH = KB / 16, RPI = 64 / CH;
-  constexpr int NW = gemm_threads(OT) / 64, ROUND = NW * RPI;
+  constexpr int NW = loader_waves(OT), ROUND = NW * RPI;
   constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
-  static_assert(NA <= 4, "band-row load instructions per stage");
-  const int w = tid >> 6, sub = (tid & 63) / CH;
+  static_assert(NA <= 8, "band-row load instructions per stage");
+  const int w = (tid >> 6) - (gemm_threads(OT) / 64 - NW), sub = (tid & 63) / CH;
+  if (w < 0) return;  // not a loader
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
     constexpr int RPW = REM / NW;
@@ -378,11 +392,28 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, in
 // The K order inside a stage is a permutation shared by both operands (lane
 // half h of an MFMA reads the same chunk indices of its A row and B row), so
 // the sum over K is unchanged.
-template <int NMB, int NNB>
+// A loader wavefront (split loads) passes NL > 0 and issue(j) for the
+// next stage's load instructions j = 0 .. NL-1, issued in NP batches at the
+// starts of evenly spaced (ks, mi) MFMA groups. Measured (Linear-1 and
+// Linear-2 together, same box): for loaders owning 4 row blocks (the
+// 256-row bands of the compute-bound Mixtral and DiT shapes) one batch at
+// the start of the stage is best (+2% and +4.6% on the GEMM against all
+// wavefronts loading before the barrier; 4 or 16 batches were 2% slower
+// than one); for loaders owning 2 (the bandwidth-bound DeepSeek-style bands
+// of about 126 rows) four batches are (+1.5%; one batch +0.4%). Each batch
+// is an ordering point for the LDS fragment reads after it, which costs the
+// MFMA-dense stages most.
+template <int NMB>
+constexpr int load_points() { return NMB >= 3 ? 1 : 4; }
+struct NoLoads {
+  __device__ void operator()(int) const {}
+};
+template <int NMB, int NNB, int NL = 0, class Issue = NoLoads>
 __device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, int tid,
-                                              f32x16 (&acc)[NMB][WaveGrid<NNB, false>::NCB]) {
+                                              f32x16 (&acc)[NMB][WaveGrid<NNB, false>::NCB],
+                                              const Issue& issue = Issue()) {
   using G = WaveGrid<NNB, false>;
-  constexpr int KB = stage_k_bytes(false);
+  constexpr int KB = stage_k_bytes(false), NG = KB / 32 * NMB;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -394,6 +425,16 @@ __device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, 
       b[nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(wave_col<NNB, false>(nb / G::CPH, nb % G::CPH, wn, lr), chunk));
 #pragma unroll
     for (int mi = 0; mi < NMB; ++mi) {
+      if constexpr (NL > 0) {
+        // issue point p of NP sits at the start of group p * NG / NP
+        constexpr int NP = load_points<NMB>() < NG ? load_points<NMB>() : NG;
+        const int g = ks * NMB + mi;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          if (g == p * NG / NP)
+#pragma unroll
+            for (int j = p * NL / NP; j < (p + 1) * NL / NP; ++j) issue(j);
+      }
       const int row = (wm + G::WM * mi) * 32 + lr;
       const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off<KB>(row, chunk));
 #pragma unroll
@@ -602,8 +643,9 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
   if constexpr (R > 0) drain<MB, NMB, NNB, OT, R - 1>(t, lds, rd + 1 == S ? 0 : rd + 1, kt + 1, tid, acc);
 }
 
-// The whole tile: every wavefront runs the same loads and barriers and owns
-// NMB of the MB row blocks; the accumulators stay inside this function.
+// The whole tile: every wavefront runs the same barriers and owns NMB of the
+// MB row blocks; the loader wavefronts also issue the ring's loads. The
+// accumulators stay inside this function.
 // The LDS ring has ring_stages(MB, NNB) stages of stage_bytes(MB, NNB): as
 // many as fit in 160 KiB (at least 2), so that S-1 stages are in flight per CU.
 // The thread index is made opaque to the optimiser at the start of the tile:
@@ -611,7 +653,13 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // are then computed once per tile instead of being hoisted, for every tile
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
-template <int MB, int NMB, int NNB, bool L1, int OT>
+// Roles of a wavefront in the K loop: every wavefront loads (ROLE_ALL), or
+// with split loads a loader (ROLE_LOADER) or not (ROLE_COMPUTE). The role is
+// a template parameter, chosen once per tile, so that each role's K loop is
+// straight-line code with its own accumulators.
+enum { ROLE_ALL = 0, ROLE_LOADER = 1, ROLE_COMPUTE = 2 };
+
+template <int MB, int NMB, int NNB, bool L1, int OT, int ROLE>
 __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, lds_t* lds, uint64_t& t_main) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
@@ -628,28 +676,55 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
   const int KT = t.ktiles;
+  static_assert((ROLE == ROLE_ALL) == !split_loads(OT), "roles follow the operand type's load split");
+  constexpr bool loader = ROLE != ROLE_COMPUTE;
   if (KT < S) {
     // the whole K extent fits in the ring
-    for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
+    if constexpr (loader)
+      for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
     wait_vmcnt<0>();
     lds_barrier();
     if constexpr (NMB > 0)
       for (int kt = 0; kt < KT; ++kt) compute_any<MB, NMB, NNB, OT>(t, lds + kt * SB, kt, tid, acc);
   } else {
+    if constexpr (loader) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
+      for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
+    }
     int rd = 0, wr = S - 1, kt = 0;
     for (; kt + S - 1 < KT; ++kt) {
-      // Slot wr held stage kt-1, which every wavefront finished reading
-      // before the barrier that closed the previous step: refill it first,
-      // so S-1 stages stay in flight while this one is awaited (the memory
-      // system bounds the requests a CU may have outstanding; letting the
-      // queue drain at every step would waste that bound).
-      issue_stage<MB, NNB, OT>(t, kt + S - 1, lds + wr * SB, tid);
-      wait_vmcnt<(S - 1) * LD>();  // this lane's loads of stage kt have landed
-      lds_barrier();               // ... everyone's
-      if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
-      lds_barrier();               // slot rd is free for the refill of the next step
+      if constexpr (split_loads(OT)) {
+        // One barrier per step. It shows stage kt complete (each loader
+        // waited for its own loads of it) and every wavefront done with
+        // stage kt-1, whose slot wr the loaders then refill while the other
+        // wavefront of their SIMD already runs this stage's MFMAs.
+        wait_vmcnt<(S - 2) * LD>();  // a loader's loads of stage kt have landed
+        lds_barrier();               // ... every loader's
+        if constexpr (ROLE == ROLE_LOADER) {
+          const int ks = kslice(t, kt + S - 1);
+          lds_t* st = lds + wr * SB;
+          if constexpr (NMB > 0) {
+            compute_stage<NMB, NNB, LD>(lds + rd * SB, lds + rd * SB + stage_a_bytes(MB, OT), tid, acc,
+                                        [&](int j) { issue_load<MB, NNB, OT>(t, ks, st, tid, j); });
+          } else {
+#pragma unroll
+            for (int j = 0; j < LD; ++j) issue_load<MB, NNB, OT>(t, ks, st, tid, j);
+          }
+        } else if constexpr (NMB > 0) {
+          compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
+        }
+      } else {
+        // Slot wr held stage kt-1, which every wavefront finished reading
+        // before the barrier that closed the previous step: refill it first,
+        // so S-1 stages stay in flight while this one is awaited (the memory
+        // system bounds the requests a CU may have outstanding; letting the
+        // queue drain at every step would waste that bound).
+        issue_stage<MB, NNB, OT>(t, kt + S - 1, lds + wr * SB, tid);
+        wait_vmcnt<(S - 1) * LD>();  // this lane's loads of stage kt have landed
+        lds_barrier();               // ... everyone's
+        if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
+        lds_barrier();               // slot rd is free for the refill of the next step
+      }
       rd = rd + 1 == S ? 0 : rd + 1;
       wr = wr + 1 == S ? 0 : wr + 1;
     }
@@ -667,15 +742,30 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
 // band fit in the LDS where 192-row ones would leave two. With four
 // wavefront rows MB is rounded up to a multiple of 4 (rows past the band
 // re-read its last row and are not stored).
-template <int MB, int NNB, bool L1, int OT>
-__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+template <int MB, int NNB, bool L1, int OT, int ROLE>
+__device__ __forceinline__ void run_tile_role(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
   constexpr int WM = WaveGrid<NNB, OT>::WM;
   if constexpr (WM == 2 && (MB & 1)) {
-    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT>(P, t, lds, t_main);
-    else tile_body<MB, MB / 2, NNB, L1, OT>(P, t, lds, t_main);
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main);
+    else tile_body<MB, MB / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main);
   } else {
     static_assert(MB % WM == 0, "row blocks per wavefront row");
-    tile_body<MB, MB / WM, NNB, L1, OT>(P, t, lds, t_main);
+    tile_body<MB, MB / WM, NNB, L1, OT, ROLE>(P, t, lds, t_main);
+  }
+}
+
+// With split loads the last loader_waves(OT) wavefronts take the loader
+// role (the wavefront index through readfirstlane, so the role test is a
+// uniform scalar branch).
+template <int MB, int NNB, bool L1, int OT>
+__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+  if constexpr (split_loads(OT)) {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= gemm_threads(OT) / 64 - loader_waves(OT))
+      run_tile_role<MB, NNB, L1, OT, ROLE_LOADER>(P, t, lds, t_main);
+    else
+      run_tile_role<MB, NNB, L1, OT, ROLE_COMPUTE>(P, t, lds, t_main);
+  } else {
+    run_tile_role<MB, NNB, L1, OT, ROLE_ALL>(P, t, lds, t_main);
   }
 }
 

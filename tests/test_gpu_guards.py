@@ -52,7 +52,8 @@ def test_offsets_past_capacity_store_nothing(sched):
         torch.cuda.synchronize()
         _expect_invalid(p, ws)
         assert torch.all(C == 7.0), bad
-        assert torch.equal(v["h"], h_before), bad
+        # bit patterns: the rows past A hold whatever the workspace held, NaNs included
+        assert torch.equal(v["h"].view(torch.int16), h_before.view(torch.int16)), bad
     # the same workspace, good offsets again
     moe.expert_forward(p, x_perm, None, v["offsets"], row_dst, g["W1"], None, g["W2"], None, C, ws)
     torch.cuda.synchronize()

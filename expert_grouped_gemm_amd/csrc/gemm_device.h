@@ -392,6 +392,11 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, in
 // The K order inside a stage is a permutation shared by both operands (lane
 // half h of an MFMA reads the same chunk indices of its A row and B row), so
 // the sum over K is unchanged.
+// The weight rows are the MFMA's A operand and the band rows its B operand,
+// so each 32x32 accumulator holds the transposed block: lane l has band row
+// l % 32 and, in elements 4q .. 4q+3, the four consecutive output columns
+// 8q + 4 (l / 32) + 0..3. The epilogue then stores four columns of one row
+// per instruction (16 bytes of fp32, 8 of bf16) instead of one.
 // A loader wavefront (split loads) passes NL > 0 and issue(j) for the
 // next stage's load instructions j = 0 .. NL-1, issued in NP batches at the
 // starts of evenly spaced (ks, mi) MFMA groups. Measured (Linear-1 and
@@ -439,7 +444,7 @@ __device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, 
       const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off<KB>(row, chunk));
 #pragma unroll
       for (int nb = 0; nb < G::NCB; ++nb)
-        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mi][nb], 0, 0, 0);
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb], a, acc[mi][nb], 0, 0, 0);
     }
   }
 }
@@ -564,17 +569,80 @@ __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int 
   }
 }
 
-// Accumulator element i of a 32x32 block sits at row 8*(i/4) + 4*(lane/32) + i%4,
-// column lane%32.
+// fp8 and MXFP4 tiles: accumulator element i of a 32x32 block sits at row
+// 8*(i/4) + 4*(lane/32) + i%4, column lane%32.
 // fp8 Linear-1 tiles of the wide width own a whole 128-column quantisation
 // block: they stage its fp32 SwiGLU values in the (free) LDS ring as
 // [rows][128] floats and quantise from there (quantize_block_lds).
 template <int NNB, bool L1, int OT>
 constexpr bool stages_block_in_lds() { return OT && L1 && NNB * 32 == 128; }
 
+// bf16 tiles: the accumulators hold transposed blocks (compute_stage), so
+// lane l owns band row l % 32 of each row block and four consecutive
+// output columns per element quad.
+template <int NMB, int NNB, bool L1>
+__device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t, int tid,
+                                              const f32x16 (&acc)[NMB][WaveGrid<NNB, OT_BF16>::NCB]) {
+  using G = WaveGrid<NNB, OT_BF16>;
+  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < NMB; ++mi) {
+    const int m = (wm + G::WM * mi) * 32 + lr;
+    if (m >= t.rows) continue;
+    if constexpr (L1) {
+      // gate block c pairs with up block c of the second half: the same SwiGLU columns
+      uint16_t* hrow = reinterpret_cast<uint16_t*>(P.H) + (size_t)(t.row0 + m) * P.f + t.n * (NNB * 32);
+#pragma unroll
+      for (int c = 0; c < G::CPH; ++c) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t packed[2];
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float g0 = acc[mi][c][4 * q + e], u0 = acc[mi][G::CPH + c][4 * q + e];
+            const float g1 = acc[mi][c][4 * q + e + 1], u1 = acc[mi][G::CPH + c][4 * q + e + 1];
+            const float a0 = g0 / (1.0f + expf(-g0)) * u0, a1 = g1 / (1.0f + expf(-g1)) * u1;
+            packed[e / 2] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+          }
+          const int col = wave_col<NNB, OT_BF16>(0, c, wn, 0) + 8 * q + 4 * hi;
+          *reinterpret_cast<uint2*>(hrow + col) = make_uint2(packed[0], packed[1]);
+        }
+      }
+    } else {
+      // a destination row outside the buffer (a caller's row_dst) is not
+      // stored but reported
+      const int dst = P.row_dst[t.row0 + m];
+      if ((unsigned)dst >= (unsigned)P.cap) {
+        __hip_atomic_fetch_or(P.meta + META_ARG_ERR, (int)ARG_ERR_ROW_DST, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        continue;
+      }
+#pragma unroll
+      for (int nb = 0; nb < G::NCB; ++nb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = t.n * (NNB * 64) + wave_col<NNB, OT_BF16>(nb / G::CPH, nb % G::CPH, wn, 0) + 8 * q + 4 * hi;
+          const float v[4] = {acc[mi][nb][4 * q], acc[mi][nb][4 * q + 1], acc[mi][nb][4 * q + 2],
+                              acc[mi][nb][4 * q + 3]};
+          if (P.c_bf16) {
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t up = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.C) + (size_t)dst * P.d + col) = make_uint2(lo, up);
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(P.C) + (size_t)dst * P.d + col) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// fp8 and MXFP4 tiles: accumulators in the MFMA's own layout (see above).
 template <int NMB, int NNB, bool L1, int OT>
-__device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
-                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
+__device__ __forceinline__ void epilogue_cols(const GemmParams& P, const Tile& t, int tid,
+                                              const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
+  static_assert(OT != OT_BF16, "bf16 tiles hold transposed blocks");
   using G = WaveGrid<NNB, OT>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
@@ -597,10 +665,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
             if constexpr (stages_block_in_lds<NNB, L1, OT>()) {
               reinterpret_cast<__attribute__((address_space(3))) float*>(lds)[m * 128 + cb] = act;
               if (P.keep_hf) P.Hf[at] = act;
-            } else if constexpr (OT) {
-              P.Hf[at] = act;  // quantised per 128-column block once both halves are stored
             } else {
-              reinterpret_cast<uint16_t*>(P.H)[at] = f32_to_bf16_rne(act);
+              P.Hf[at] = act;  // quantised per 128-column block once both halves are stored
             }
           }
         } else {
@@ -629,6 +695,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int
       }
     }
   }
+}
+
+template <int NMB, int NNB, bool L1, int OT>
+__device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
+                                         const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
+  if constexpr (OT == OT_BF16) epilogue_rows<NMB, NNB, L1>(P, t, tid, acc);
+  else epilogue_cols<NMB, NNB, L1, OT>(P, t, tid, acc, lds);
 }
 
 // Drain the last R+1 stages of the ring: stage kt is complete once at most R

@@ -459,7 +459,9 @@ __device__ __forceinline__ i32x8 lds_read_32B(const lds_t* base, int row, int ch
 // sum (two v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales) is
 // promoted into the fp32 accumulator with the row's activation scale times
 // the weight block's scale: acc += partial * sx[row] * sw, with sw = swg for
-// the first half of the weight rows and swu for the second.
+// the first half of the weight rows and swu for the second. As in the bf16
+// stage, the weight rows are the MFMA's A operand, so the accumulators hold
+// transposed blocks (a lane has one band row).
 template <int NMB, int NNB>
 __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* sb, const lds_t* ss, float swg,
                                                   float swu, int tid, f32x16 (&acc)[NMB][WaveGrid<NNB, true>::NCB]) {
@@ -479,21 +481,17 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
         // weight fragments are read per row block, not kept: with two
         // wavefronts per SIMD a wavefront has 256 registers
         const i32x8 b = lds_read_32B(sb, wave_col<NNB, true>(nb / G::CPH, nb % G::CPH, wn, lr), ks * 4 + hi * 2);
-        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, ks ? part[nb] : zero, 0, 0, 0, 127, 0, 127);
+        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, ks ? part[nb] : zero, 0, 0, 0, 127, 0, 127);
       }
     }
-    // the lane's rows of block mb: mb*32 + 8*g + 4*hi + (0..3), g = 0..3
+    // transposed blocks (weights as the A operand): the lane's one row of
+    // block mb is mb*32 + lr, so one activation scale serves all 16 elements
+    const float sx = *(const lds_f32*)(ss + (mb * 32 + lr) * 4);
+    const float sg = sx * swg, su = sx * swu;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 sx = *(const lds_f32x4*)(ss + (mb * 32 + 8 * g + 4 * hi) * 4);
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-#pragma unroll
-        for (int nb = 0; nb < G::NCB; ++nb)
-          acc[mi][nb][i] = fmaf(part[nb][i], sx[j] * (nb < G::CPH ? swg : swu), acc[mi][nb][i]);
-      }
-    }
+      for (int nb = 0; nb < G::NCB; ++nb) acc[mi][nb][i] = fmaf(part[nb][i], nb < G::CPH ? sg : su, acc[mi][nb][i]);
   }
 }
 
@@ -506,9 +504,11 @@ __device__ __forceinline__ void compute_stage_fp8(const lds_t* sa, const lds_t* 
 // the e4m3 operand and its next 16 with [32 + 16h, +16), so the activation
 // fragment of lane half h is chunks h and 2 + h of the step (16 bytes each),
 // not chunks 2h and 2h + 1 as in the fp8 x fp8 product. (Measured on gfx950
-// with one-hot products.) The activation side runs at unit scale and the
-// stage's partial sum is promoted with the row's fp32 activation scale:
-// acc += partial * sx[row].
+// with one-hot products, the 4-bit operand in the B position; the pairing is
+// the operand formats', and holds with the 4-bit operand as A, where it sits
+// now for the transposed accumulators: the W4A8 parity tests compare every
+// element.) The activation side runs at unit scale and the stage's partial
+// sum is promoted with the row's fp32 activation scale: acc += partial * sx.
 template <int NMB, int NNB>
 __device__ __forceinline__ void compute_stage_w4(const lds_t* sa, const lds_t* sb, const lds_t* ss, int tid,
                                                  f32x16 (&acc)[NMB][WaveGrid<NNB, OT_W4A8>::NCB]) {
@@ -537,19 +537,17 @@ __device__ __forceinline__ void compute_stage_w4(const lds_t* sa, const lds_t* s
         const i32x4 q = *(const lds_i32x4*)(sb + lds_off<64>(row, ks * 2 + hi));
         const i32x8 b = {q[0], q[1], q[2], q[3], 0, 0, 0, 0};
         const int sc = (sw[nb] >> (8 * (ks * 2 + hi))) & 0xFF;
-        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, ks ? part[nb] : zero, 0, 4, 0, 127, 0, sc);
+        // the E2M1 weights as the A operand (cbsz = 4, with their E8M0
+        // scale), the e4m3 activations as B (blgp = 0, unit scale)
+        part[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, ks ? part[nb] : zero, 4, 0, 0, sc, 0, 127);
       }
     }
+    // transposed blocks: one activation scale (row mb*32 + lr) per lane
+    const float sx = *(const lds_f32*)(ss + (mb * 32 + lr) * 4);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 sx = *(const lds_f32x4*)(ss + (mb * 32 + 8 * g + 4 * hi) * 4);
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-#pragma unroll
-        for (int nb = 0; nb < G::NCB; ++nb) acc[mi][nb][i] = fmaf(part[nb][i], sx[j], acc[mi][nb][i]);
-      }
-    }
+      for (int nb = 0; nb < G::NCB; ++nb) acc[mi][nb][i] = fmaf(part[nb][i], sx, acc[mi][nb][i]);
   }
 }
 
@@ -569,28 +567,53 @@ __device__ __forceinline__ void compute_any(const Tile& t, const lds_t* st, int 
   }
 }
 
-// fp8 and MXFP4 tiles: accumulator element i of a 32x32 block sits at row
-// 8*(i/4) + 4*(lane/32) + i%4, column lane%32.
-// fp8 Linear-1 tiles of the wide width own a whole 128-column quantisation
-// block: they stage its fp32 SwiGLU values in the (free) LDS ring as
-// [rows][128] floats and quantise from there (quantize_block_lds).
+// Whether a Linear-1 tile owns whole 128-column quantisation blocks of H
+// (e4m3 H, wide tiles) and stages them in LDS.
 template <int NNB, bool L1, int OT>
 constexpr bool stages_block_in_lds() { return OT && L1 && NNB * 32 == 128; }
 
-// bf16 tiles: the accumulators hold transposed blocks (compute_stage), so
-// lane l owns band row l % 32 of each row block and four consecutive
-// output columns per element quad.
-template <int NMB, int NNB, bool L1>
+// The accumulators hold transposed blocks (the compute stages take the
+// weight rows as the MFMA's A operand), so lane l owns band row l % 32 of
+// each row block and, in elements 4q .. 4q+3, four consecutive output
+// columns 8q + 4 (l / 32) + 0..3.
+// fp8 / MXFP4 Linear-1 tiles of the wide width own a whole 128-column
+// quantisation block: they stage its fp32 SwiGLU values in the (free) LDS
+// ring as [rows][128] floats and quantise from there (quantize_block_from);
+// narrow ones store them to H_f32 and pair up through blk_done.
+template <int NMB, int NNB, bool L1, int OT>
 __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t, int tid,
-                                              const f32x16 (&acc)[NMB][WaveGrid<NNB, OT_BF16>::NCB]) {
-  using G = WaveGrid<NNB, OT_BF16>;
+                                              const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
+  using G = WaveGrid<NNB, OT>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int mi = 0; mi < NMB; ++mi) {
     const int m = (wm + G::WM * mi) * 32 + lr;
     if (m >= t.rows) continue;
-    if constexpr (L1) {
+    if constexpr (L1 && OT != OT_BF16) {
+      // gate block c pairs with up block c of the second half: the same SwiGLU columns
+      float* frow = P.Hf + (size_t)(t.row0 + m) * P.f + t.n * (NNB * 32);
+#pragma unroll
+      for (int c = 0; c < G::CPH; ++c) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = acc[mi][c][4 * q + e], u = acc[mi][G::CPH + c][4 * q + e];
+            a[e] = g / (1.0f + expf(-g)) * u;
+          }
+          const int cb = wave_col<NNB, OT>(0, c, wn, 0) + 8 * q + 4 * hi;
+          const float4 v = make_float4(a[0], a[1], a[2], a[3]);
+          if constexpr (stages_block_in_lds<NNB, L1, OT>()) {
+            *reinterpret_cast<lds_f32x4*>(lds + (m * 128 + cb) * 4) = f32x4{a[0], a[1], a[2], a[3]};
+            if (P.keep_hf) *reinterpret_cast<float4*>(frow + cb) = v;
+          } else {
+            *reinterpret_cast<float4*>(frow + cb) = v;  // quantised once both halves are stored
+          }
+        }
+      }
+    } else if constexpr (L1) {
       // gate block c pairs with up block c of the second half: the same SwiGLU columns
       uint16_t* hrow = reinterpret_cast<uint16_t*>(P.H) + (size_t)(t.row0 + m) * P.f + t.n * (NNB * 32);
 #pragma unroll
@@ -605,7 +628,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t
             const float a0 = g0 / (1.0f + expf(-g0)) * u0, a1 = g1 / (1.0f + expf(-g1)) * u1;
             packed[e / 2] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
           }
-          const int col = wave_col<NNB, OT_BF16>(0, c, wn, 0) + 8 * q + 4 * hi;
+          const int col = wave_col<NNB, OT>(0, c, wn, 0) + 8 * q + 4 * hi;
           *reinterpret_cast<uint2*>(hrow + col) = make_uint2(packed[0], packed[1]);
         }
       }
@@ -621,7 +644,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t
       for (int nb = 0; nb < G::NCB; ++nb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = t.n * (NNB * 64) + wave_col<NNB, OT_BF16>(nb / G::CPH, nb % G::CPH, wn, 0) + 8 * q + 4 * hi;
+          const int col = t.n * (NNB * 64) + wave_col<NNB, OT>(nb / G::CPH, nb % G::CPH, wn, 0) + 8 * q + 4 * hi;
           const float v[4] = {acc[mi][nb][4 * q], acc[mi][nb][4 * q + 1], acc[mi][nb][4 * q + 2],
                               acc[mi][nb][4 * q + 3]};
           if (P.c_bf16) {
@@ -638,70 +661,10 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t
   }
 }
 
-// fp8 and MXFP4 tiles: accumulators in the MFMA's own layout (see above).
-template <int NMB, int NNB, bool L1, int OT>
-__device__ __forceinline__ void epilogue_cols(const GemmParams& P, const Tile& t, int tid,
-                                              const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
-  static_assert(OT != OT_BF16, "bf16 tiles hold transposed blocks");
-  using G = WaveGrid<NNB, OT>;
-  const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
-  const int lr = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int mi = 0; mi < NMB; ++mi) {
-    const int mb = wm + G::WM * mi;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-      if (m < t.rows) {
-        if constexpr (L1) {
-          // gate block c pairs with up block c of the second half: the same SwiGLU columns
-#pragma unroll
-          for (int c = 0; c < G::CPH; ++c) {
-            const float g = acc[mi][c][i], u = acc[mi][G::CPH + c][i];
-            const float act = g / (1.0f + expf(-g)) * u;
-            const int cb = wave_col<NNB, OT>(0, c, wn, lr);
-            const int col = t.n * (NNB * 32) + cb;
-            const size_t at = (size_t)(t.row0 + m) * P.f + col;
-            if constexpr (stages_block_in_lds<NNB, L1, OT>()) {
-              reinterpret_cast<__attribute__((address_space(3))) float*>(lds)[m * 128 + cb] = act;
-              if (P.keep_hf) P.Hf[at] = act;
-            } else {
-              P.Hf[at] = act;  // quantised per 128-column block once both halves are stored
-            }
-          }
-        } else {
-          // a destination row outside the buffer (a caller's row_dst) is not
-          // stored but reported
-          const int dst = P.row_dst[t.row0 + m];
-          if ((unsigned)dst < (unsigned)P.cap) {
-            if (P.c_bf16) {
-#pragma unroll
-              for (int nb = 0; nb < G::NCB; ++nb) {
-                const int col = t.n * (NNB * 64) + wave_col<NNB, OT>(nb / G::CPH, nb % G::CPH, wn, lr);
-                reinterpret_cast<uint16_t*>(P.C)[(size_t)dst * P.d + col] = f32_to_bf16_rne(acc[mi][nb][i]);
-              }
-            } else {
-#pragma unroll
-              for (int nb = 0; nb < G::NCB; ++nb) {
-                const int col = t.n * (NNB * 64) + wave_col<NNB, OT>(nb / G::CPH, nb % G::CPH, wn, lr);
-                reinterpret_cast<float*>(P.C)[(size_t)dst * P.d + col] = acc[mi][nb][i];
-              }
-            }
-          } else {
-            __hip_atomic_fetch_or(P.meta + META_ARG_ERR, (int)ARG_ERR_ROW_DST, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-    }
-  }
-}
-
 template <int NMB, int NNB, bool L1, int OT>
 __device__ __forceinline__ void epilogue(const GemmParams& P, const Tile& t, int tid,
                                          const f32x16 (&acc)[NMB][WaveGrid<NNB, OT>::NCB], lds_t* lds) {
-  if constexpr (OT == OT_BF16) epilogue_rows<NMB, NNB, L1>(P, t, tid, acc);
-  else epilogue_cols<NMB, NNB, L1, OT>(P, t, tid, acc, lds);
+  epilogue_rows<NMB, NNB, L1, OT>(P, t, tid, acc, lds);
 }
 
 // Drain the last R+1 stages of the ring: stage kt is complete once at most R

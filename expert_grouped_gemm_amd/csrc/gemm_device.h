@@ -199,15 +199,16 @@ __host__ __device__ constexpr int ring_stages(int MB, int NNB, int OT) {
 // Wavefronts that issue the ring's global -> LDS loads. The CU accepts about
 // one such 1 KiB instruction per 22 cycles, so a 64 KiB stage takes about
 // 1400 cycles to issue, and a wavefront blocked at an issue runs no MFMA.
-// bf16: one wavefront per SIMD (the last four) issues the whole stage, after
-// the step's barrier, while the other wavefront of its SIMD already runs its
+// One wavefront per SIMD (the last four) issues the whole stage, after the
+// step's barrier, while the other wavefront of its SIMD already runs its
 // MFMAs. With every wavefront issuing its share before the barrier, the
 // issue and the MFMAs ran one after the other: per-phase cycle counts of
 // the Mixtral Linear-1 K loop gave 17-33% of each step to issuing and 12-20%
-// to the barrier behind it, against 1.5% waiting for data. The fp8 and
-// MXFP4 kernels, whose wavefronts use the whole register file, keep every
-// wavefront issuing (the loaders' extra row registers would spill).
-__host__ __device__ constexpr int loader_waves(int OT) { return OT == OT_BF16 ? 4 : gemm_threads(OT) / 64; }
+// to the barrier behind it, against 1.5% waiting for data. MXFP4 tiles
+// split the same way (the W4A8 share's GEMM 358 -> 316 us). The fp8 kernel
+// keeps every wavefront issuing: at its 256-register budget the loaders'
+// row addresses spill inside the K loop, and the split measured 1% slower.
+__host__ __device__ constexpr int loader_waves(int OT) { return OT == OT_FP8 ? gemm_threads(OT) / 64 : 4; }
 __host__ __device__ constexpr bool split_loads(int OT) { return loader_waves(OT) < gemm_threads(OT) / 64; }
 
 // global -> LDS loads issued per loader lane per stage (16 bytes each, plus
@@ -739,12 +740,14 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
         if constexpr (ROLE == ROLE_LOADER) {
           const int ks = kslice(t, kt + S - 1);
           lds_t* st = lds + wr * SB;
-          if constexpr (NMB > 0) {
+          if constexpr (NMB > 0 && OT == OT_BF16) {
             compute_stage<NMB, NNB, LD>(lds + rd * SB, lds + rd * SB + stage_a_bytes(MB, OT), tid, acc,
                                         [&](int j) { issue_load<MB, NNB, OT>(t, ks, st, tid, j); });
           } else {
+            // e4m3 activations: the whole stage at once, then the MFMAs
 #pragma unroll
             for (int j = 0; j < LD; ++j) issue_load<MB, NNB, OT>(t, ks, st, tid, j);
+            if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
           }
         } else if constexpr (NMB > 0) {
           compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);

@@ -690,6 +690,24 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // are then computed once per tile instead of being hoisted, for every tile
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
+// Cross-tile prefetch (bf16 tiles of at most four row blocks, separate
+// schedule): a tile whose successor on the same workgroup has its shape (row
+// blocks and width) issues the successor's first ring stages after its own
+// K loop, before its epilogue, so that the stores and the next loads
+// overlap. Measured (same box): the DeepSeek-style share's GEMM (bands of
+// about 126 rows) 589 -> 583 us; on 256-row tiles it paid nothing (DiT: the
+// Linear-2 epilogue slowed from 10.8 to 11.4 us, its stores queued behind
+// the loads, as much as the K loop gained) or lost (Mixtral's GEMM 1.8%
+// slower), so those tiles do not prefetch. `next` is the
+// successor if `has_next`, `issued` reports whether its stages were issued,
+// `pre` tells a tile that its own first stages are already in flight.
+struct Chain {
+  Tile next;
+  bool has_next = false;
+  bool pre = false;
+  bool issued = false;
+};
+
 // Roles of a wavefront in the K loop: every wavefront loads (ROLE_ALL), or
 // with split loads a loader (ROLE_LOADER) or not (ROLE_COMPUTE). The role is
 // a template parameter, chosen once per tile, so that each role's K loop is
@@ -697,7 +715,8 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 enum { ROLE_ALL = 0, ROLE_LOADER = 1, ROLE_COMPUTE = 2 };
 
 template <int MB, int NMB, int NNB, bool L1, int OT, int ROLE>
-__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, lds_t* lds, uint64_t& t_main) {
+__device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, lds_t* lds, uint64_t& t_main,
+                                          Chain& ch) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   Tile t = t0;
@@ -715,18 +734,25 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
   const int KT = t.ktiles;
   static_assert((ROLE == ROLE_ALL) == !split_loads(OT), "roles follow the operand type's load split");
   constexpr bool loader = ROLE != ROLE_COMPUTE;
+  // A tile whose first stages its predecessor issued waits for all of them
+  // (and the predecessor's epilogue stores, issued after them) at once.
+  if (ch.pre) wait_vmcnt<0>();
   if (KT < S) {
     // the whole K extent fits in the ring
-    if constexpr (loader)
-      for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
+    if constexpr (loader) {
+      if (!ch.pre)
+        for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
+    }
     wait_vmcnt<0>();
     lds_barrier();
     if constexpr (NMB > 0)
       for (int kt = 0; kt < KT; ++kt) compute_any<MB, NMB, NNB, OT>(t, lds + kt * SB, kt, tid, acc);
   } else {
     if constexpr (loader) {
+      if (!ch.pre) {
 #pragma unroll
-      for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
+        for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
+      }
     }
     int rd = 0, wr = S - 1, kt = 0;
     for (; kt + S - 1 < KT; ++kt) {
@@ -771,6 +797,24 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
   }
   lds_barrier();  // LDS ring free for the next tile
   if (P.trace) t_main = __builtin_amdgcn_s_memrealtime();
+  if constexpr (OT == OT_BF16 && MB <= 4) {
+    // the successor's first stages, if it has this tile's shape (the bf16
+    // epilogue leaves the LDS alone, so the ring is free from here on)
+    if (ch.has_next) {
+      const Tile& n0 = ch.next;
+      constexpr int WM = WaveGrid<NNB, OT>::WM;
+      const int nmb = WM == 2 ? min((n0.rows + 31) >> 5, 8) : (n0.rows <= 128 ? 4 : 8);
+      if (n0.nnb == NNB && nmb == MB) {
+        if constexpr (loader) {
+          Tile tn = n0;
+          fill_arow<MB, NNB, OT>(tn, tid);
+          const int ns = tn.ktiles < S ? tn.ktiles : S - 1;
+          for (int s = 0; s < ns; ++s) issue_stage<MB, NNB, OT>(tn, s, lds + s * SB, tid);
+        }
+        ch.issued = true;
+      }
+    }
+  }
   if constexpr (NMB > 0) epilogue<NMB, NNB, L1, OT>(P, t, tid, acc, lds);
 }
 
@@ -782,14 +826,15 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
 // wavefront rows MB is rounded up to a multiple of 4 (rows past the band
 // re-read its last row and are not stored).
 template <int MB, int NNB, bool L1, int OT, int ROLE>
-__device__ __forceinline__ void run_tile_role(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+__device__ __forceinline__ void run_tile_role(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
+                                              Chain& ch) {
   constexpr int WM = WaveGrid<NNB, OT>::WM;
   if constexpr (WM == 2 && (MB & 1)) {
-    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main);
-    else tile_body<MB, MB / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main);
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
+    else tile_body<MB, MB / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
   } else {
     static_assert(MB % WM == 0, "row blocks per wavefront row");
-    tile_body<MB, MB / WM, NNB, L1, OT, ROLE>(P, t, lds, t_main);
+    tile_body<MB, MB / WM, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
   }
 }
 
@@ -797,34 +842,36 @@ __device__ __forceinline__ void run_tile_role(const GemmParams& P, const Tile& t
 // role (the wavefront index through readfirstlane, so the role test is a
 // uniform scalar branch).
 template <int MB, int NNB, bool L1, int OT>
-__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+__device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
+                                         Chain& ch) {
   if constexpr (split_loads(OT)) {
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= gemm_threads(OT) / 64 - loader_waves(OT))
-      run_tile_role<MB, NNB, L1, OT, ROLE_LOADER>(P, t, lds, t_main);
+      run_tile_role<MB, NNB, L1, OT, ROLE_LOADER>(P, t, lds, t_main, ch);
     else
-      run_tile_role<MB, NNB, L1, OT, ROLE_COMPUTE>(P, t, lds, t_main);
+      run_tile_role<MB, NNB, L1, OT, ROLE_COMPUTE>(P, t, lds, t_main, ch);
   } else {
-    run_tile_role<MB, NNB, L1, OT, ROLE_ALL>(P, t, lds, t_main);
+    run_tile_role<MB, NNB, L1, OT, ROLE_ALL>(P, t, lds, t_main, ch);
   }
 }
 
 template <int NNB, bool L1, int OT>
-__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main) {
+__device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
+                                              Chain& ch) {
   if constexpr (WaveGrid<NNB, OT>::WM == 2) {
     switch ((t.rows + 31) >> 5) {
-      case 1: run_tile<1, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 2: run_tile<2, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 3: run_tile<3, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 4: run_tile<4, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 5: run_tile<5, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 6: run_tile<6, NNB, L1, OT>(P, t, lds, t_main); break;
-      case 7: run_tile<7, NNB, L1, OT>(P, t, lds, t_main); break;
-      default: run_tile<8, NNB, L1, OT>(P, t, lds, t_main); break;
+      case 1: run_tile<1, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 2: run_tile<2, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 3: run_tile<3, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 4: run_tile<4, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 5: run_tile<5, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 6: run_tile<6, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 7: run_tile<7, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      default: run_tile<8, NNB, L1, OT>(P, t, lds, t_main, ch); break;
     }
   } else {
     static_assert(WaveGrid<NNB, OT>::WM == 4, "wavefront rows");
-    if (t.rows <= 128) run_tile<4, NNB, L1, OT>(P, t, lds, t_main);
-    else run_tile<8, NNB, L1, OT>(P, t, lds, t_main);
+    if (t.rows <= 128) run_tile<4, NNB, L1, OT>(P, t, lds, t_main, ch);
+    else run_tile<8, NNB, L1, OT>(P, t, lds, t_main, ch);
   }
 }
 
@@ -1009,10 +1056,8 @@ __device__ __forceinline__ void record_tile(const GemmParams& P, bool l1, int p,
 }
 
 template <bool L1, int OT>
-__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int nnb, bool fused, lds_t* lds) {
+__device__ __forceinline__ Tile make_tile(const GemmParams& P, int p, int n, int nnb) {
   constexpr int esz = OT ? 1 : 2;
-  uint64_t t_start = 0, t_ready = 0, t_main = 0;
-  if (P.trace) t_start = __builtin_amdgcn_s_memrealtime();
   Tile t;
   const int e = P.band_expert[p];
   t.row0 = P.band_row0[p];
@@ -1067,11 +1112,22 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
       t.Sg = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn) / 128) * (P.f >> 7);
       t.Su = P.W2s + ((size_t)e * (P.d >> 7) + (n * bn + bn / 2) / 128) * (P.f >> 7);
     }
+  }
+  return t;
+}
+
+template <bool L1, int OT>
+__device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int nnb, bool fused, lds_t* lds,
+                                        Chain& ch) {
+  uint64_t t_start = 0, t_ready = 0, t_main = 0;
+  if (P.trace) t_start = __builtin_amdgcn_s_memrealtime();
+  const Tile t = make_tile<L1, OT>(P, p, n, nnb);
+  if constexpr (!L1) {
     if (fused) wait_row_ready(P, p);
   }
   if (P.trace) t_ready = __builtin_amdgcn_s_memrealtime();
-  if (nnb == 4) dispatch_tile<4, L1, OT>(P, t, lds, t_main);
-  else dispatch_tile<2, L1, OT>(P, t, lds, t_main);
+  if (nnb == 4) dispatch_tile<4, L1, OT>(P, t, lds, t_main, ch);
+  else dispatch_tile<2, L1, OT>(P, t, lds, t_main, ch);
   if constexpr (L1) finish_l1_tile<OT>(P, t, p, fused, lds);
   if constexpr (!L1) {
     if (P.row_done) finish_l2_tile(P, t);
@@ -1104,16 +1160,32 @@ __device__ __forceinline__ void separate_tiles(const GemmParams& P, int nb, int 
   const int total = nb * N;
   const int cut = (nnb == 4 && total % G) ? total / G * G : total;
   const int end = cut + 2 * (total - cut);
-  int p, n;
-  for (int i = lid; i < end; i += G) {
+  // tile i of the list: band, N-tile and width
+  auto coords = [&](int i, int& p, int& n, int& w) {
     if (i < cut) {
       raster(i, nb, N, P.group_m, p, n);
-      do_tile<L1, OT>(P, p, n, nnb, false, lds);
+      w = nnb;
     } else {
       const int j = i - cut;
       raster(cut + (j >> 1), nb, N, P.group_m, p, n);
-      do_tile<L1, OT>(P, p, 2 * n + (j & 1), 2, false, lds);
+      n = 2 * n + (j & 1);
+      w = 2;
     }
+  };
+  bool pre = false;
+  for (int i = lid; i < end; i += G) {
+    int p, n, w;
+    coords(i, p, n, w);
+    Chain ch;
+    ch.pre = pre;
+    if (OT == OT_BF16 && i + G < end) {
+      int p2, n2, w2;
+      coords(i + G, p2, n2, w2);
+      ch.next = make_tile<L1, OT>(P, p2, n2, w2);
+      ch.has_next = true;
+    }
+    do_tile<L1, OT>(P, p, n, w, false, lds, ch);
+    pre = ch.issued;
   }
 }
 
@@ -1128,6 +1200,7 @@ __global__ __launch_bounds__(gemm_threads(OT), 1) void moe_gemm_kernel(GemmParam
   const int lid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   const int Pb = P.meta[META_P];
   int p, n;
+  Chain none;  // the fused schedules prefetch nothing across tiles
   switch (P.mode) {
     case MODE_SEP_L1:
       separate_tiles<true, OT>(P, Pb, P.N1, P.nnb1, lid, G, lds);
@@ -1141,11 +1214,11 @@ __global__ __launch_bounds__(gemm_threads(OT), 1) void moe_gemm_kernel(GemmParam
         const int pb0 = P.wave_band0[wv], pb1 = P.wave_band0[wv + 1];
         for (int i = lid; i < (pb1 - pb0) * P.N1; i += G) {
           raster(i, pb1 - pb0, P.N1, P.group_m, p, n);
-          do_tile<true, OT>(P, pb0 + p, n, P.nnb1, true, lds);
+          do_tile<true, OT>(P, pb0 + p, n, P.nnb1, true, lds, none);
         }
         for (int i = lid; i < (pb1 - pb0) * P.N2; i += G) {
           raster(i, pb1 - pb0, P.N2, P.group_m, p, n);
-          do_tile<false, OT>(P, pb0 + p, n, P.nnb2, true, lds);
+          do_tile<false, OT>(P, pb0 + p, n, P.nnb2, true, lds, none);
         }
       }
       break;
@@ -1168,13 +1241,13 @@ __global__ __launch_bounds__(gemm_threads(OT), 1) void moe_gemm_kernel(GemmParam
         if (k2 < cut2) raster(k2, Pb, P2, P.group_m, p2, c2);
         if (k2 < cut2 && p2 + P.lead_D <= b1) {
           const int n = 2 * c2 + r;
-          if (n < P.N2) do_tile<false, OT>(P, p2, n, P.nnb2, true, lds);
+          if (n < P.N2) do_tile<false, OT>(P, p2, n, P.nnb2, true, lds, none);
           k2 += Gp;
         } else {
           int p1, c1;
           raster(k1, Pb, P1, P.group_m, p1, c1);
           const int n = 2 * c1 + r;
-          if (n < P.N1) do_tile<true, OT>(P, p1, n, P.nnb1, true, lds);
+          if (n < P.N1) do_tile<true, OT>(P, p1, n, P.nnb1, true, lds, none);
           k1 += Gp;
         }
       }
@@ -1186,7 +1259,7 @@ __global__ __launch_bounds__(gemm_threads(OT), 1) void moe_gemm_kernel(GemmParam
       for (int j = lid; j < 4 * (end2 - cut2); j += G) {
         int p2, c2;
         raster(cut2 + (j >> 2), Pb, P2, P.group_m, p2, c2);
-        if (2 * c2 + ((j >> 1) & 1) < P.N2) do_tile<false, OT>(P, p2, 4 * c2 + (j & 3), 2, true, lds);
+        if (2 * c2 + ((j >> 1) & 1) < P.N2) do_tile<false, OT>(P, p2, 4 * c2 + (j & 3), 2, true, lds, none);
       }
       break;
     }

@@ -157,9 +157,12 @@ struct Tile {
   // (which then points at X); null: row row0 + r
   const int32_t* a_src;
   int a_k;
-  // the A rows this lane loads, one per band-row load instruction of a stage
-  // (filled at the start of the tile, once its row-block count is known)
-  int arow[8];
+  // byte offset from A of the row this lane loads, one per band-row load
+  // instruction of a stage (filled at the start of the tile, once its
+  // row-block count is known). The ring loads address a uniform base plus a
+  // 32-bit per-lane offset (the instructions' SGPR-base form, one VGPR per
+  // load instead of two).
+  uint32_t arow[8];
 };
 
 // Operand types of the expert GEMM (the template parameter OT): bf16
@@ -298,21 +301,24 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
   constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
   constexpr int NBW = NNB * 64 / ROUNDB, half = NNB * 32;
   static_assert(NBW * ROUNDB == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
-  const int w = (tid >> 6) - (gemm_threads(OT) / 64 - NW), lane = tid & 63;
+  // (the wavefront index as a scalar: every instruction's rows then lie in
+  // one half of the weight rows, whose base is a uniform choice)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) - (gemm_threads(OT) / 64 - NW), lane = tid & 63;
   if (j < NA) {
     constexpr int RPW = REM / NW;  // rows per wavefront in the partial round
     const int sub = lane / CH, slot = lane % CH;
     const bool part = REM && j == NAF;
     const int r0 = part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI;
     const int r = r0 + sub;
-    const uint8_t* g = t.A + (size_t)t.arow[j] * t.lda + kt * KB + ((slot ^ chunk_swizzle<KB>(r)) << 4);
+    const uint8_t* g = t.A + (t.arow[j] + (uint32_t)(kt * KB + ((slot ^ chunk_swizzle<KB>(r)) << 4)));
     if (!part || sub < RPW) __builtin_amdgcn_global_load_lds(g, st + r0 * KB, 16, 0, 0);
   } else if (j < NA + NBW) {
     const int sub = lane / CHB, slot = lane % CHB;
     const int r0 = ((j - NA) * NW + w) * RPIB;
     const int r = r0 + sub;
-    const uint8_t* base = r < half ? t.Bg : t.Bu;
-    const uint8_t* g = base + (size_t)(r & (half - 1)) * t.ldb + kt * KBB + ((slot ^ chunk_swizzle<KBB>(r)) << 4);
+    const uint8_t* base = r0 < half ? t.Bg : t.Bu;
+    const uint8_t* g =
+        base + (uint32_t)((r & (half - 1)) * (uint32_t)t.ldb + kt * KBB + ((slot ^ chunk_swizzle<KBB>(r)) << 4));
     __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, OT) + r0 * KBB, 16, 0, 0);
   } else if constexpr (OT != OT_BF16) {
     lds_t* ss = st + stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT);
@@ -321,15 +327,15 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
       constexpr int PER = kBM / NW;
       const int r = w * PER + lane;
       const int gr = r < t.rows ? r : t.rows - 1;
-      const float* g = t.As + (size_t)kt * t.cap_stride + gr;
+      const float* g = t.As + (uint32_t)(kt * (uint32_t)t.cap_stride + gr);
       if (lane < PER) __builtin_amdgcn_global_load_lds(g, ss + w * PER * 4, 4, 0, 0);
     } else if constexpr (mxfp4_weights(OT)) {
       // the weight rows' E8M0 scales of this stage: one dword (four 32-wide
       // blocks) per weight row, NNB * 64 / NW rows per wavefront
       constexpr int PERB = NNB * 64 / NW;
       const int r = w * PERB + lane;
-      const uint8_t* base = r < half ? t.Eg : t.Eu;
-      const uint8_t* g = base + (size_t)(r & (half - 1)) * t.epitch + kt * 4;
+      const uint8_t* base = w * PERB < half ? t.Eg : t.Eu;
+      const uint8_t* g = base + (uint32_t)((r & (half - 1)) * (uint32_t)t.epitch + kt * 4);
       if (lane < PERB) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4 + w * PERB * 4, 4, 0, 0);
     } else {
       // the block's two weight scales (first and second half of the weight
@@ -359,7 +365,11 @@ __device__ __forceinline__ void fill_arow(Tile& t, int tid) {
     const bool part = REM && j == NAF;
     const int r = (part ? NAF * ROUND + w * RPW : (j * NW + w) * RPI) + sub;
     const int gr = r < t.rows ? r : t.rows - 1;
-    t.arow[j] = t.a_src ? t.a_src[t.row0 + gr] / t.a_k : t.row0 + gr;
+    // gathered: X row a_src[row0 + r] / k from X; else band row r from the
+    // band's first row (t.A points there). 32 bits suffice: the problem
+    // limits keep cap * d and cap * f (cap >= T) below 2^31 elements of at
+    // most 2 bytes.
+    t.arow[j] = (uint32_t)(t.a_src ? t.a_src[t.row0 + gr] / t.a_k : gr) * (uint32_t)t.lda;
   }
 }
 
@@ -1071,7 +1081,9 @@ __device__ __forceinline__ Tile make_tile(const GemmParams& P, int p, int n, int
     const int bn = nnb * 32;  // SwiGLU columns: bn gate rows and bn up rows
     t.lda = (size_t)P.d * esz;
     t.ldb = W4 ? (size_t)P.d / 2 : (size_t)P.d * esz;
-    t.A = P.X;  // rows by t.arow: X_perm row row0 + r, or X row a_src[row0 + r] / k
+    // rows by t.arow: X row a_src[row0 + r] / k from X itself, or X_perm row
+    // row0 + r from the band's first row
+    t.A = P.a_src ? P.X : P.X + (size_t)t.row0 * t.lda;
     t.a_src = P.a_src;
     t.a_k = P.a_k;
     const uint8_t* We = P.W1 + (size_t)e * 2 * P.f * t.ldb;
@@ -1095,7 +1107,7 @@ __device__ __forceinline__ Tile make_tile(const GemmParams& P, int p, int n, int
     const int bn = nnb * 64;  // output columns
     t.lda = (size_t)P.f * esz;
     t.ldb = W4 ? (size_t)P.f / 2 : (size_t)P.f * esz;
-    t.A = P.H;
+    t.A = P.H + (size_t)t.row0 * t.lda;
     t.a_src = nullptr;
     t.a_k = 1;
     t.Bg = P.W2 + ((size_t)e * P.d + (size_t)n * bn) * t.ldb;

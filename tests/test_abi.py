@@ -55,6 +55,8 @@ GOOD = dict(T=64, d=128, f=256, E_global=4, k=2)
     (dict(k=17, E_global=32), 2), (dict(k=5, E_global=4), 2), (dict(E_global=2048, k=2), 2),
     (dict(d=100), 2), (dict(f=192), 2), (dict(T=0), 2), (dict(e_begin=3, e_end=3), 2),
     (dict(e_begin=0, e_end=5), 2), (dict(num_segments=3), 2),
+    # cap * d past 2^31 elements: the kernels' 32-bit row and byte offsets
+    (dict(T=1 << 21, d=1024), 2),
 ])
 def test_unsupported_shapes(L, over, code):
     kw = dict(GOOD)

@@ -207,11 +207,11 @@ __host__ __device__ constexpr int ring_stages(int MB, int NNB, int OT) {
 // MFMAs. With every wavefront issuing its share before the barrier, the
 // issue and the MFMAs ran one after the other: per-phase cycle counts of
 // the Mixtral Linear-1 K loop gave 17-33% of each step to issuing and 12-20%
-// to the barrier behind it, against 1.5% waiting for data. MXFP4 tiles
-// split the same way (the W4A8 share's GEMM 358 -> 316 us). The fp8 kernel
-// keeps every wavefront issuing: at its 256-register budget the loaders'
-// row addresses spill inside the K loop, and the split measured 1% slower.
-__host__ __device__ constexpr int loader_waves(int OT) { return OT == OT_FP8 ? gemm_threads(OT) / 64 : 4; }
+// to the barrier behind it, against 1.5% waiting for data. Every operand
+// type splits this way: W4A8 share GEMM 358 -> 316 us, fp8 381 -> 372 us
+// (fp8 only once the loads' addresses became 32-bit offsets; with 64-bit
+// addresses its loaders spilled inside the K loop and the split lost 1%).
+__host__ __device__ constexpr int loader_waves(int) { return 4; }
 __host__ __device__ constexpr bool split_loads(int OT) { return loader_waves(OT) < gemm_threads(OT) / 64; }
 
 // global -> LDS loads issued per loader lane per stage (16 bytes each, plus

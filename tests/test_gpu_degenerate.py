@@ -96,3 +96,39 @@ def test_router_widths_and_large_expert_counts(name):
     np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
     np.testing.assert_array_equal(v["row_dst"].numpy()[:A], ref["row_dst"])
     check_y(Y.float().cpu().numpy(), ref["Y"], Y32.cpu().numpy(), label=name)
+
+
+def test_dispatch_scan_of_a_long_token_batch():
+    """T = 100000: each of the scan's 16 wavefronts owns 6272 output rows,
+    far more than its registers hold, so the scan walks its segment in
+    passes, and the last segment is ragged. Routing and the whole dispatch,
+    from the fused call and from the component calls, bit for bit against
+    the oracle."""
+    import expert_grouped_gemm_amd as moe
+    cfg = moe_synth.make_config("tiny", T=100000, d=128, f=128, E_global=64, k=4, e_begin=8, e_end=40,
+                                num_segments=4, seed=61)
+    print("[degenerate] T=100000 dispatch", flush=True)
+    inp = moe_synth.generate(cfg)
+    idx, w, _ = oracle.route_topk(inp["logits"].numpy(), cfg.k)
+    ref = oracle.dispatch(idx, w, cfg.e_begin, cfg.e_end, cfg.num_segments)
+    A = ref["A"]
+    g = to_gpu(inp)
+    p = problem_of(cfg, sched="auto")
+    _, _, ws = run_layer(p, g, want_fp32=False)
+    moe.check_workspace(p, ws)
+    v = {k: t.cpu() for k, t in moe.workspace_views(p, ws).items() if k not in ("x_perm", "h", "combine_buf")}
+    np.testing.assert_array_equal(v["topk_idx"].numpy(), idx)
+    for key in ("counts", "offsets", "tok_off"):
+        np.testing.assert_array_equal(v[key].numpy(), ref[key], err_msg=key)
+    np.testing.assert_array_equal(v["row_src"].numpy()[:A], ref["row_src"])
+    np.testing.assert_array_equal(v["row_dst"].numpy()[:A], ref["row_dst"])
+    # the component dispatch's scan kernel on the same routing
+    ws2 = moe.alloc_workspace(p)
+    v2 = moe.workspace_views(p, ws2)
+    moe.dispatch(p, g["X"], None, v["topk_idx"].cuda(), v["topk_w"].cuda(), v2["counts"], v2["offsets"],
+                 v2["row_src"], v2["row_dst"], v2["tok_off"], v2["comb_w"], v2["x_perm"], None, ws2)
+    torch.cuda.synchronize()
+    moe.check_workspace(p, ws2)
+    for key in ("counts", "offsets", "tok_off"):
+        np.testing.assert_array_equal(v2[key].cpu().numpy(), ref[key], err_msg=key)
+    np.testing.assert_array_equal(v2["row_src"].cpu().numpy()[:A], ref["row_src"])

@@ -410,15 +410,17 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, in
 // per instruction (16 bytes of fp32, 8 of bf16) instead of one.
 // A loader wavefront (split loads) passes NL > 0 and issue(j) for the
 // next stage's load instructions j = 0 .. NL-1, issued in NP batches at the
-// starts of evenly spaced (ks, mi) MFMA groups. Measured (Linear-1 and
+// starts of evenly spaced K steps. Measured (Linear-1 and
 // Linear-2 together, same box): for loaders owning 4 row blocks (the
 // 256-row bands of the compute-bound Mixtral and DiT shapes) one batch at
 // the start of the stage is best (+2% and +4.6% on the GEMM against all
 // wavefronts loading before the barrier; 4 or 16 batches were 2% slower
 // than one); for loaders owning 2 (the bandwidth-bound DeepSeek-style bands
 // of about 126 rows) four batches are (+1.5%; one batch +0.4%). Each batch
-// is an ordering point for the LDS fragment reads after it, which costs the
-// MFMA-dense stages most.
+// is an ordering point for the LDS fragment reads after it, so the stage
+// reads K step ks+1's fragments into a second register set before the batch
+// and the MFMAs of step ks: Mixtral 1050 -> 1106 TFLOP/s, the DiT GEMM 1920
+// -> 1856 us against fragments read just in time.
 template <int NMB>
 constexpr int load_points() { return NMB >= 3 ? 1 : 4; }
 struct NoLoads {
@@ -429,34 +431,38 @@ __device__ __forceinline__ void compute_stage(const lds_t* sa, const lds_t* sb, 
                                               f32x16 (&acc)[NMB][WaveGrid<NNB, false>::NCB],
                                               const Issue& issue = Issue()) {
   using G = WaveGrid<NNB, false>;
-  constexpr int KB = stage_k_bytes(false), NG = KB / 32 * NMB;
+  constexpr int KB = stage_k_bytes(false), NKS = KB / 32;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < KB / 32; ++ks) {
+  // fragments of K step ks+1 are read before the load batch and the MFMAs of
+  // step ks, so no load issue stands between a fragment read and its MFMA
+  bf16x8 fb[2][G::NCB], fa[2][NMB];
+  auto read = [&](int ks, int buf) {
     const int chunk = ks * 2 + hi;
-    bf16x8 b[G::NCB];
 #pragma unroll
     for (int nb = 0; nb < G::NCB; ++nb)
-      b[nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(wave_col<NNB, false>(nb / G::CPH, nb % G::CPH, wn, lr), chunk));
+      fb[buf][nb] = *(const lds_bf16x8*)(sb + lds_off<KB>(wave_col<NNB, false>(nb / G::CPH, nb % G::CPH, wn, lr), chunk));
 #pragma unroll
-    for (int mi = 0; mi < NMB; ++mi) {
-      if constexpr (NL > 0) {
-        // issue point p of NP sits at the start of group p * NG / NP
-        constexpr int NP = load_points<NMB>() < NG ? load_points<NMB>() : NG;
-        const int g = ks * NMB + mi;
+    for (int mi = 0; mi < NMB; ++mi)
+      fa[buf][mi] = *(const lds_bf16x8*)(sa + lds_off<KB>((wm + G::WM * mi) * 32 + lr, chunk));
+  };
+  read(0, 0);
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-          if (g == p * NG / NP)
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks + 1 < NKS) read(ks + 1, (ks + 1) & 1);
+    if constexpr (NL > 0) {
+      constexpr int NP = load_points<NMB>() < NKS ? load_points<NMB>() : NKS;
 #pragma unroll
-            for (int j = p * NL / NP; j < (p + 1) * NL / NP; ++j) issue(j);
-      }
-      const int row = (wm + G::WM * mi) * 32 + lr;
-      const bf16x8 a = *(const lds_bf16x8*)(sa + lds_off<KB>(row, chunk));
+      for (int p = 0; p < NP; ++p)
+        if (ks == p * NKS / NP)
+#pragma unroll
+          for (int j = p * NL / NP; j < (p + 1) * NL / NP; ++j) issue(j);
+    }
+#pragma unroll
+    for (int mi = 0; mi < NMB; ++mi)
 #pragma unroll
       for (int nb = 0; nb < G::NCB; ++nb)
-        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nb], a, acc[mi][nb], 0, 0, 0);
-    }
+        acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][nb], fa[ks & 1][mi], acc[mi][nb], 0, 0, 0);
   }
 }
 

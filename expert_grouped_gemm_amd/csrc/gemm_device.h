@@ -144,6 +144,7 @@ struct Tile {
   int nnb;                // width: NNB * 64 weight rows
   int ktiles;             // K bytes / stage_k_bytes
   int krot;               // pipeline stage kt streams K slice (kt + krot) mod ktiles
+  bool once;              // the expert's only row band: each weight byte is read once per launch
   // fp8 activations only
   const float* As;        // row scales of K block 0 for the band's first row (next block: + cap)
   const float* Sg;        // fp8 weights: block scales of the first half along K (one per 128-byte stage)
@@ -212,7 +213,21 @@ __host__ __device__ constexpr int ring_stages(int MB, int NNB, int OT) {
 // (fp8 only once the loads' addresses became 32-bit offsets; with 64-bit
 // addresses its loaders spilled inside the K loop and the split lost 1%).
 __host__ __device__ constexpr int loader_waves(int) { return 4; }
-__host__ __device__ constexpr bool split_loads(int OT) { return loader_waves(OT) < gemm_threads(OT) / 64; }
+
+// Weight rows of an expert with a single row band are read once per launch:
+// no other tile of the launch reads them again. Their ring loads then carry
+// the non-temporal hint, so that the weight stream does not displace what is
+// reused (the band rows, H, the combine buffer) from the L2 and the
+// last-level cache. Measured on the DeepSeek-style share (every expert one
+// band): Linear-1 365 -> 332 us, Linear-2 220 -> 211 us, fp8 GEMM 362 -> 330
+// us; the counted L2 misses were the same, the hint changed what the misses
+// cost. On experts with several bands (Mixtral, DiT) the hint made every
+// launch slower (4-5%): their weights are read again by the other bands.
+// MXFP4 weight rows are excluded: a stage takes 64 bytes of a row, half a
+// 128-byte line, and the next stage the other half, which a streamed line no
+// longer holds (the W4A8 share's Linear-1 183 -> 191 us with the hint).
+__host__ __device__ constexpr bool streams_once(int OT) { return stage_kb_bytes(OT) == 128; }
+constexpr int kCpolNT = 2;  // cache-policy operand of the global -> LDS load: nt
 
 // global -> LDS loads issued per loader lane per stage (16 bytes each, plus
 // one 4-byte row-scale load with fp8)
@@ -287,8 +302,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 16-byte instruction lands at LDS base + 16*i (64/CH rows of KB bytes, CH =
 // KB/16 chunks per row), lane i of a 4-byte instruction at base + 4*i.
 // issue_load issues instruction j of the stage; only the loader wavefronts
-// call it (w below is the loader index).
-template <int MB, int NNB, int OT>
+// call it (w below is the loader index). NT: the weight rows are loaded
+// non-temporally (see streams_once).
+template <int MB, int NNB, int OT, bool NT>
 __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int tid, int j) {
   constexpr int KB = stage_k_bytes(OT), CH = KB / 16, RPI = 64 / CH;
   constexpr int NW = loader_waves(OT), ROUND = NW * RPI;
@@ -319,7 +335,7 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
     const uint8_t* base = r0 < half ? t.Bg : t.Bu;
     const uint8_t* g =
         base + (uint32_t)((r & (half - 1)) * (uint32_t)t.ldb + kt * KBB + ((slot ^ chunk_swizzle<KBB>(r)) << 4));
-    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, OT) + r0 * KBB, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, st + stage_a_bytes(MB, OT) + r0 * KBB, 16, 0, NT ? kCpolNT : 0);
   } else if constexpr (OT != OT_BF16) {
     lds_t* ss = st + stage_a_bytes(MB, OT) + stage_b_bytes(NNB, OT);
     if (j == NA + NBW) {
@@ -391,11 +407,11 @@ __device__ __forceinline__ int kslice(const Tile& t, int kt) {
   return s >= t.ktiles ? s - t.ktiles : s;
 }
 
-template <int MB, int NNB, int OT>
+template <int MB, int NNB, int OT, bool NT>
 __device__ __forceinline__ void issue_stage(const Tile& t, int kt, lds_t* st, int tid) {
   const int ks = kslice(t, kt);
 #pragma unroll
-  for (int j = 0; j < stage_loads(MB, NNB, OT); ++j) issue_load<MB, NNB, OT>(t, ks, st, tid, j);
+  for (int j = 0; j < stage_loads(MB, NNB, OT); ++j) issue_load<MB, NNB, OT, NT>(t, ks, st, tid, j);
 }
 
 // MFMAs of one stage for a wavefront that owns NMB row blocks {wm, wm+2, ...}
@@ -702,7 +718,7 @@ __device__ __forceinline__ void drain(const Tile& t, lds_t* lds, int rd, int kt,
 // The LDS ring has ring_stages(MB, NNB) stages of stage_bytes(MB, NNB): as
 // many as fit in 160 KiB (at least 2), so that S-1 stages are in flight per CU.
 // The thread index is made opaque to the optimiser at the start of the tile:
-// the per-lane address offsets derived from it (64-bit row * pitch products)
+// the per-lane address offsets derived from it (row * pitch products)
 // are then computed once per tile instead of being hoisted, for every tile
 // shape of the persistent loop at once, to the kernel entry where they would
 // stay live (and spill) for the whole launch.
@@ -724,13 +740,12 @@ struct Chain {
   bool issued = false;
 };
 
-// Roles of a wavefront in the K loop: every wavefront loads (ROLE_ALL), or
-// with split loads a loader (ROLE_LOADER) or not (ROLE_COMPUTE). The role is
-// a template parameter, chosen once per tile, so that each role's K loop is
-// straight-line code with its own accumulators.
-enum { ROLE_ALL = 0, ROLE_LOADER = 1, ROLE_COMPUTE = 2 };
+// Roles of a wavefront in the K loop: a loader (ROLE_LOADER) or not
+// (ROLE_COMPUTE). The role is a template parameter, chosen once per tile, so
+// that each role's K loop is straight-line code with its own accumulators.
+enum { ROLE_LOADER = 1, ROLE_COMPUTE = 2 };
 
-template <int MB, int NMB, int NNB, bool L1, int OT, int ROLE>
+template <int MB, int NMB, int NNB, bool L1, int OT, int ROLE, bool NT>
 __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, lds_t* lds, uint64_t& t_main,
                                           Chain& ch) {
   int tid = threadIdx.x;
@@ -748,8 +763,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
   const int KT = t.ktiles;
-  static_assert((ROLE == ROLE_ALL) == !split_loads(OT), "roles follow the operand type's load split");
-  constexpr bool loader = ROLE != ROLE_COMPUTE;
+  constexpr bool loader = ROLE == ROLE_LOADER;
   // A tile whose first stages its predecessor issued waits for all of them
   // (and the predecessor's epilogue stores, issued after them) at once.
   if (ch.pre) wait_vmcnt<0>();
@@ -757,7 +771,7 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
     // the whole K extent fits in the ring
     if constexpr (loader) {
       if (!ch.pre)
-        for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT>(t, kt, lds + kt * SB, tid);
+        for (int kt = 0; kt < KT; ++kt) issue_stage<MB, NNB, OT, NT>(t, kt, lds + kt * SB, tid);
     }
     wait_vmcnt<0>();
     lds_barrier();
@@ -767,44 +781,34 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
     if constexpr (loader) {
       if (!ch.pre) {
 #pragma unroll
-        for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT>(t, s, lds + s * SB, tid);
+        for (int s = 0; s < S - 1; ++s) issue_stage<MB, NNB, OT, NT>(t, s, lds + s * SB, tid);
       }
     }
     int rd = 0, wr = S - 1, kt = 0;
     for (; kt + S - 1 < KT; ++kt) {
-      if constexpr (split_loads(OT)) {
-        // One barrier per step. It shows stage kt complete (each loader
-        // waited for its own loads of it) and every wavefront done with
-        // stage kt-1, whose slot wr the loaders then refill while the other
-        // wavefront of their SIMD already runs this stage's MFMAs.
-        wait_vmcnt<(S - 2) * LD>();  // a loader's loads of stage kt have landed
-        lds_barrier();               // ... every loader's
-        if constexpr (ROLE == ROLE_LOADER) {
-          const int ks = kslice(t, kt + S - 1);
-          lds_t* st = lds + wr * SB;
-          if constexpr (NMB > 0 && OT == OT_BF16) {
-            compute_stage<NMB, NNB, LD>(lds + rd * SB, lds + rd * SB + stage_a_bytes(MB, OT), tid, acc,
-                                        [&](int j) { issue_load<MB, NNB, OT>(t, ks, st, tid, j); });
-          } else {
-            // e4m3 activations: the whole stage at once, then the MFMAs
+      // One barrier per step. It shows stage kt complete (each loader waited
+      // for its own loads of it) and every wavefront done with stage kt-1,
+      // whose slot wr the loaders then refill while the other wavefront of
+      // their SIMD already runs this stage's MFMAs. (With every wavefront
+      // issuing its share of the refill before the step's wait, a second
+      // barrier closed each step and the issue and the MFMAs ran one after
+      // the other: see loader_waves.)
+      wait_vmcnt<(S - 2) * LD>();  // a loader's loads of stage kt have landed
+      lds_barrier();               // ... every loader's
+      if constexpr (loader) {
+        const int ks = kslice(t, kt + S - 1);
+        lds_t* st = lds + wr * SB;
+        if constexpr (NMB > 0 && OT == OT_BF16) {
+          compute_stage<NMB, NNB, LD>(lds + rd * SB, lds + rd * SB + stage_a_bytes(MB, OT), tid, acc,
+                                      [&](int j) { issue_load<MB, NNB, OT, NT>(t, ks, st, tid, j); });
+        } else {
+          // e4m3 activations: the whole stage at once, then the MFMAs
 #pragma unroll
-            for (int j = 0; j < LD; ++j) issue_load<MB, NNB, OT>(t, ks, st, tid, j);
-            if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
-          }
-        } else if constexpr (NMB > 0) {
-          compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
+          for (int j = 0; j < LD; ++j) issue_load<MB, NNB, OT, NT>(t, ks, st, tid, j);
+          if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
         }
-      } else {
-        // Slot wr held stage kt-1, which every wavefront finished reading
-        // before the barrier that closed the previous step: refill it first,
-        // so S-1 stages stay in flight while this one is awaited (the memory
-        // system bounds the requests a CU may have outstanding; letting the
-        // queue drain at every step would waste that bound).
-        issue_stage<MB, NNB, OT>(t, kt + S - 1, lds + wr * SB, tid);
-        wait_vmcnt<(S - 1) * LD>();  // this lane's loads of stage kt have landed
-        lds_barrier();               // ... everyone's
-        if constexpr (NMB > 0) compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
-        lds_barrier();               // slot rd is free for the refill of the next step
+      } else if constexpr (NMB > 0) {
+        compute_any<MB, NMB, NNB, OT>(t, lds + rd * SB, kt, tid, acc);
       }
       rd = rd + 1 == S ? 0 : rd + 1;
       wr = wr + 1 == S ? 0 : wr + 1;
@@ -820,12 +824,12 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
       const Tile& n0 = ch.next;
       constexpr int WM = WaveGrid<NNB, OT>::WM;
       const int nmb = WM == 2 ? min((n0.rows + 31) >> 5, 8) : (n0.rows <= 128 ? 4 : 8);
-      if (n0.nnb == NNB && nmb == MB) {
+      if (n0.nnb == NNB && nmb == MB && (streams_once(OT) && n0.once) == NT) {
         if constexpr (loader) {
           Tile tn = n0;
           fill_arow<MB, NNB, OT>(tn, tid);
           const int ns = tn.ktiles < S ? tn.ktiles : S - 1;
-          for (int s = 0; s < ns; ++s) issue_stage<MB, NNB, OT>(tn, s, lds + s * SB, tid);
+          for (int s = 0; s < ns; ++s) issue_stage<MB, NNB, OT, NT>(tn, s, lds + s * SB, tid);
         }
         ch.issued = true;
       }
@@ -841,53 +845,49 @@ __device__ __forceinline__ void tile_body(const GemmParams& P, const Tile& t0, l
 // band fit in the LDS where 192-row ones would leave two. With four
 // wavefront rows MB is rounded up to a multiple of 4 (rows past the band
 // re-read its last row and are not stored).
-template <int MB, int NNB, bool L1, int OT, int ROLE>
+template <int MB, int NNB, bool L1, int OT, int ROLE, bool NT>
 __device__ __forceinline__ void run_tile_role(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
                                               Chain& ch) {
   constexpr int WM = WaveGrid<NNB, OT>::WM;
   if constexpr (WM == 2 && (MB & 1)) {
-    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
-    else tile_body<MB, MB / 2, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
+    if (((threadIdx.x >> 6) % WM) == 0) tile_body<MB, (MB + 1) / 2, NNB, L1, OT, ROLE, NT>(P, t, lds, t_main, ch);
+    else tile_body<MB, MB / 2, NNB, L1, OT, ROLE, NT>(P, t, lds, t_main, ch);
   } else {
     static_assert(MB % WM == 0, "row blocks per wavefront row");
-    tile_body<MB, MB / WM, NNB, L1, OT, ROLE>(P, t, lds, t_main, ch);
+    tile_body<MB, MB / WM, NNB, L1, OT, ROLE, NT>(P, t, lds, t_main, ch);
   }
 }
 
-// With split loads the last loader_waves(OT) wavefronts take the loader
-// role (the wavefront index through readfirstlane, so the role test is a
-// uniform scalar branch).
-template <int MB, int NNB, bool L1, int OT>
+// The last loader_waves(OT) wavefronts take the loader role (the wavefront
+// index through readfirstlane, so the role test is a uniform scalar branch).
+template <int MB, int NNB, bool L1, int OT, bool NT>
 __device__ __forceinline__ void run_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
                                          Chain& ch) {
-  if constexpr (split_loads(OT)) {
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= gemm_threads(OT) / 64 - loader_waves(OT))
-      run_tile_role<MB, NNB, L1, OT, ROLE_LOADER>(P, t, lds, t_main, ch);
-    else
-      run_tile_role<MB, NNB, L1, OT, ROLE_COMPUTE>(P, t, lds, t_main, ch);
-  } else {
-    run_tile_role<MB, NNB, L1, OT, ROLE_ALL>(P, t, lds, t_main, ch);
-  }
+  static_assert(loader_waves(OT) < gemm_threads(OT) / 64, "loaders and compute-only wavefronts");
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= gemm_threads(OT) / 64 - loader_waves(OT))
+    run_tile_role<MB, NNB, L1, OT, ROLE_LOADER, NT>(P, t, lds, t_main, ch);
+  else
+    run_tile_role<MB, NNB, L1, OT, ROLE_COMPUTE, NT>(P, t, lds, t_main, ch);
 }
 
-template <int NNB, bool L1, int OT>
+template <int NNB, bool L1, int OT, bool NT>
 __device__ __forceinline__ void dispatch_tile(const GemmParams& P, const Tile& t, lds_t* lds, uint64_t& t_main,
                                               Chain& ch) {
   if constexpr (WaveGrid<NNB, OT>::WM == 2) {
     switch ((t.rows + 31) >> 5) {
-      case 1: run_tile<1, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 2: run_tile<2, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 3: run_tile<3, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 4: run_tile<4, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 5: run_tile<5, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 6: run_tile<6, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      case 7: run_tile<7, NNB, L1, OT>(P, t, lds, t_main, ch); break;
-      default: run_tile<8, NNB, L1, OT>(P, t, lds, t_main, ch); break;
+      case 1: run_tile<1, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 2: run_tile<2, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 3: run_tile<3, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 4: run_tile<4, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 5: run_tile<5, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 6: run_tile<6, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      case 7: run_tile<7, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
+      default: run_tile<8, NNB, L1, OT, NT>(P, t, lds, t_main, ch); break;
     }
   } else {
     static_assert(WaveGrid<NNB, OT>::WM == 4, "wavefront rows");
-    if (t.rows <= 128) run_tile<4, NNB, L1, OT>(P, t, lds, t_main, ch);
-    else run_tile<8, NNB, L1, OT>(P, t, lds, t_main, ch);
+    if (t.rows <= 128) run_tile<4, NNB, L1, OT, NT>(P, t, lds, t_main, ch);
+    else run_tile<8, NNB, L1, OT, NT>(P, t, lds, t_main, ch);
   }
 }
 
@@ -1075,7 +1075,8 @@ template <bool L1, int OT>
 __device__ __forceinline__ Tile make_tile(const GemmParams& P, int p, int n, int nnb) {
   constexpr int esz = OT ? 1 : 2;
   Tile t;
-  const int e = P.band_expert[p];
+  const int eb = P.band_expert[p], e = eb & kBandExpertMask;
+  t.once = (eb & kBandSingle) != 0;
   t.row0 = P.band_row0[p];
   t.rows = P.band_rows[p];
   t.n = n;
@@ -1144,8 +1145,17 @@ __device__ __forceinline__ void do_tile(const GemmParams& P, int p, int n, int n
     if (fused) wait_row_ready(P, p);
   }
   if (P.trace) t_ready = __builtin_amdgcn_s_memrealtime();
-  if (nnb == 4) dispatch_tile<4, L1, OT>(P, t, lds, t_main, ch);
-  else dispatch_tile<2, L1, OT>(P, t, lds, t_main, ch);
+  bool nt = false;
+  if constexpr (streams_once(OT)) nt = t.once;
+  if (nt) {
+    if constexpr (streams_once(OT)) {
+      if (nnb == 4) dispatch_tile<4, L1, OT, true>(P, t, lds, t_main, ch);
+      else dispatch_tile<2, L1, OT, true>(P, t, lds, t_main, ch);
+    }
+  } else {
+    if (nnb == 4) dispatch_tile<4, L1, OT, false>(P, t, lds, t_main, ch);
+    else dispatch_tile<2, L1, OT, false>(P, t, lds, t_main, ch);
+  }
   if constexpr (L1) finish_l1_tile<OT>(P, t, p, fused, lds);
   if constexpr (!L1) {
     if (P.row_done) finish_l2_tile(P, t);

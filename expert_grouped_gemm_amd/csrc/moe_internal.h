@@ -36,6 +36,12 @@ enum MetaSlot {
 // the dispatch's report survives until moe_check_workspace reads it.
 enum ArgErr { ARG_ERR_DISPATCH_CAP = 1, ARG_ERR_OFFSETS = 2, ARG_ERR_ROW_DST = 4, ARG_ERR_ALL = 7 };
 
+// band_expert[p] of the band table: the band's local expert, plus
+// kBandSingle if the band is its expert's only one (the expert has at most
+// kBM rows, so every weight byte of the expert is read by this band alone).
+constexpr int32_t kBandSingle = 1 << 30;
+constexpr int32_t kBandExpertMask = kBandSingle - 1;
+
 enum GemmMode { MODE_SEP_L1 = 0, MODE_SEP_L2 = 1, MODE_WAVE = 2, MODE_INTERLEAVED = 3 };
 
 // Spin limit of a Linear-2 tile waiting for its row's Linear-1 tiles (each

@@ -144,7 +144,7 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ offsets, i
       __syncthreads();
     }
     if (q < Ptot) {
-      band_expert[pos] = ex;
+      band_expert[pos] = ex | (row_off[ex + 1] - row_off[ex] <= kBM ? kBandSingle : 0);
       band_row0[pos] = r0;
       band_rows[pos] = rows;
     }

@@ -83,7 +83,7 @@ def gemm_bytes(cfg, counts, cbuf_esz=4) -> float:
     return float(w + rows)
 
 
-GEMM_SOURCES = ("gemm_device.h", "plan_device.h", "gemm.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_w4a8.hip")
+GEMM_SOURCES = ("gemm_device.h", "plan_device.h", "moe_internal.h", "gemm.hip", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_w4a8.hip")
 
 
 def gemm_source_digest():

@@ -630,6 +630,17 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t
   using G = WaveGrid<NNB, OT>;
   const int lane = tid & 63, w = tid >> 6, wm = w % G::WM, wn = w / G::WM;
   const int lr = lane & 31, hi = lane >> 5;
+  // Linear-2: every row's destination is loaded before the first store. As
+  // far as the compiler knows a store may alias row_dst, so a load placed
+  // after one waits for a memory round trip of its own, once per row block.
+  int dsts[NMB];
+  if constexpr (!L1) {
+#pragma unroll
+    for (int mi = 0; mi < NMB; ++mi) {
+      const int m = (wm + G::WM * mi) * 32 + lr;
+      dsts[mi] = m < t.rows ? P.row_dst[t.row0 + m] : 0;
+    }
+  }
 #pragma unroll
   for (int mi = 0; mi < NMB; ++mi) {
     const int m = (wm + G::WM * mi) * 32 + lr;
@@ -679,7 +690,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& P, const Tile& t
     } else {
       // a destination row outside the buffer (a caller's row_dst) is not
       // stored but reported
-      const int dst = P.row_dst[t.row0 + m];
+      const int dst = dsts[mi];
       if ((unsigned)dst >= (unsigned)P.cap) {
         __hip_atomic_fetch_or(P.meta + META_ARG_ERR, (int)ARG_ERR_ROW_DST, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         continue;

@@ -229,10 +229,11 @@ __host__ __device__ constexpr int loader_waves(int) { return 4; }
 __host__ __device__ constexpr bool streams_once(int OT) { return stage_kb_bytes(OT) == 128; }
 constexpr int kCpolNT = 2;  // cache-policy operand of the global -> LDS load: nt
 
-// global -> LDS loads issued per loader lane per stage (16 bytes each, plus
-// one 4-byte row-scale load with fp8)
-// (band rows: a whole number of instructions per wavefront plus, when they
-// do not divide evenly, one partial instruction in every wavefront)
+// global -> LDS loads issued per loader lane per stage: 16 bytes each, plus
+// two 4-byte loads with e4m3 activations (the row scales and the weight
+// scales). The band rows take a whole number of instructions per loader
+// wavefront plus, when they do not divide evenly, one partial instruction in
+// every loader wavefront.
 __host__ __device__ constexpr int stage_a_rows_per_round(int OT) {
   return loader_waves(OT) * 64 * 16 / stage_k_bytes(OT);
 }
@@ -313,7 +314,7 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
   constexpr int KBB = stage_kb_bytes(OT), CHB = KBB / 16, RPIB = 64 / CHB, ROUNDB = NW * RPIB;
   static_assert(ROUNDB == stage_b_rows_per_round(OT), "weight rows per load round");
   // NAF full rounds of band rows, then REM rows (a multiple of 32) spread over
-  // all wavefronts: REM / NW rows each, the other lanes idle
+  // the loader wavefronts: REM / NW rows each, the other lanes idle
   constexpr int NAF = MB * 32 / ROUND, REM = MB * 32 - NAF * ROUND, NA = NAF + (REM ? 1 : 0);
   constexpr int NBW = NNB * 64 / ROUNDB, half = NNB * 32;
   static_assert(NBW * ROUNDB == NNB * 64 && REM % NW == 0 && REM / NW <= RPI, "stage rows per wavefront");
@@ -355,8 +356,8 @@ __device__ __forceinline__ void issue_load(const Tile& t, int kt, lds_t* st, int
       if (lane < PERB) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4 + w * PERB * 4, 4, 0, 0);
     } else {
       // the block's two weight scales (first and second half of the weight
-      // rows) after the row scales. Every wavefront loads them, the same 8
-      // bytes, so that all wavefronts issue the same number of loads per
+      // rows) after the row scales. Every loader wavefront loads them, the
+      // same 8 bytes, so that all loaders issue the same number of loads per
       // stage; kept in the stage, they need no scalar load in the MFMA loop.
       const float* g = lane == 0 ? t.Sg + kt : t.Su + kt;
       if (lane < 2) __builtin_amdgcn_global_load_lds(g, ss + kBM * 4, 4, 0, 0);
